@@ -213,7 +213,7 @@ def prefill_rows(q, k, v, gate, layer: LayerSpec, rows):
         key = (b, kv)
         if key not in rotated:
             kk = np.asarray(k[b, :, kv], dtype=np.float64)
-            rotated[key] = rope(kk, np.arange(T, dtype=np.float64)[:, None],
+            rotated[key] = rope(kk, np.arange(T, dtype=np.float64),
                                 layer.rope_theta, r)
         qi = rope(np.asarray(q[b, t, h], dtype=np.float64), float(t),
                   layer.rope_theta, r)
