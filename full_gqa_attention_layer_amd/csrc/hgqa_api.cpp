@@ -1,0 +1,277 @@
+// C-ABI front end of libhgqa.so: argument checks, RoPE frequency set-up and
+// dispatch to the gfx950 kernels. Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/hgqa.h"
+#include "hgqa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return HGQA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct Layer {
+  int sliding, window, Hq, G, Hkv, D, rdims, half;
+  float theta, scale;
+  hgqa::Elem elem;
+  size_t esize;
+};
+
+// Validates a layer descriptor; fills `out`. Returns HGQA_OK or an error.
+int check_layer(const hgqa_layer* L, Layer* out) {
+  if (!L) return fail(HGQA_EINVAL, "layer descriptor is NULL");
+  if (L->layer_type != HGQA_FULL && L->layer_type != HGQA_SLIDING)
+    return fail(HGQA_EINVAL, "layer_type %d is neither HGQA_FULL nor HGQA_SLIDING", L->layer_type);
+  if (L->layer_type == HGQA_SLIDING && L->window < 1)
+    return fail(HGQA_EINVAL, "a sliding layer needs window >= 1 (got %d)", L->window);
+  if (L->num_q_heads < 1) return fail(HGQA_EINVAL, "num_q_heads must be >= 1");
+  if (L->gqa_ratio < 1) return fail(HGQA_EINVAL, "gqa_ratio must be >= 1");
+  if (L->num_q_heads % L->gqa_ratio)
+    return fail(HGQA_EINVAL, "num_q_heads %d is not a multiple of gqa_ratio %d", L->num_q_heads,
+                L->gqa_ratio);
+  if (L->dtype != HGQA_BF16 && L->dtype != HGQA_FP32)
+    return fail(HGQA_EINVAL, "dtype %d is neither HGQA_BF16 nor HGQA_FP32", L->dtype);
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(HGQA_EUNSUPPORTED, "head_dim %d is not supported (64 or 128)", L->head_dim);
+  if (!std::isfinite(L->rope_theta) || L->rope_theta < 0.0f)
+    return fail(HGQA_EINVAL, "rope_theta must be finite and >= 0");
+  if (!std::isfinite(L->rotary_fraction) || L->rotary_fraction < 0.0f || L->rotary_fraction > 1.0f)
+    return fail(HGQA_EINVAL, "rotary_fraction must lie in [0, 1]");
+  if (!std::isfinite(L->softmax_scale)) return fail(HGQA_EINVAL, "softmax_scale is not finite");
+  Layer& o = *out;
+  o.sliding = L->layer_type == HGQA_SLIDING;
+  o.window = o.sliding ? L->window : 0;
+  o.Hq = L->num_q_heads;
+  o.G = L->gqa_ratio;
+  o.Hkv = o.Hq / o.G;
+  o.D = L->head_dim;
+  o.theta = L->rope_theta;
+  o.elem = L->dtype == HGQA_BF16 ? hgqa::Elem::BF16 : hgqa::Elem::F32;
+  o.esize = L->dtype == HGQA_BF16 ? 2 : 4;
+  int r = (int)std::lround((double)L->rotary_fraction * o.D);
+  if (o.theta == 0.0f) r = 0;
+  if (r % 2) return fail(HGQA_EINVAL, "rotary dims round(f*D) = %d must be even", r);
+  if (o.elem == hgqa::Elem::BF16 && r % 16)
+    return fail(HGQA_EUNSUPPORTED, "bf16 layers need rotary dims %% 16 == 0 (got %d)", r);
+  o.rdims = r;
+  o.half = r / 2;
+  o.scale = L->softmax_scale > 0.0f ? L->softmax_scale : (float)(1.0 / std::sqrt((double)o.D));
+  return HGQA_OK;
+}
+
+void fill_rope(const Layer& l, hgqa::RopeArgs* r) {
+  std::memset(r, 0, sizeof *r);
+  r->half = l.half;
+  r->rdims = l.rdims;
+  for (int i = 0; i < l.half; ++i)
+    r->freq_over_pi[i] = std::pow((double)l.theta, -2.0 * i / l.rdims) / M_PI;
+}
+
+// Largest element count any one buffer may hold; keeps 64-bit offsets exact
+// and block counts within the grid limit.
+constexpr long long kMaxElems = 1LL << 40;
+
+size_t prefill_ws(const Layer& l, int B, int T) {
+  return round256((size_t)B * l.Hkv * T * l.D * l.esize) + round256((size_t)T * l.half * sizeof(float2));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hgqa_last_error(void) { return g_last_error.c_str(); }
+
+size_t attn_prefill_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t seq_len) {
+  Layer l;
+  if (check_layer(layer, &l) != HGQA_OK || batch < 0 || seq_len < 0) return 0;
+  return prefill_ws(l, batch, seq_len);
+}
+
+int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const void* q,
+                 const void* k, const void* v, const void* gate, void* out, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  Layer l;
+  int rc = check_layer(layer, &l);
+  if (rc != HGQA_OK) return rc;
+  if (batch < 0 || seq_len < 0) return fail(HGQA_EINVAL, "batch and seq_len must be >= 0");
+  if (batch == 0 || seq_len == 0) return ok();
+  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
+  if ((long long)batch * seq_len * l.Hq * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "problem too large");
+  const long long TG = (long long)seq_len * l.G;
+  if (l.elem == hgqa::Elem::BF16 && (TG + 127) / 128 * batch * l.Hkv > 0x7fffffffLL)
+    return fail(HGQA_EUNSUPPORTED, "too many query blocks");
+  if (!q || !k || !v || !gate || !out || !workspace)
+    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return fail(HGQA_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
+  const size_t need = prefill_ws(l, batch, seq_len);
+  if (workspace_bytes < need)
+    return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (out == q || out == k || out == v || out == gate)
+    return fail(HGQA_EINVAL, "out must not alias an input");
+
+  hgqa::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.out = out;
+  a.k_rot = workspace;
+  a.cs_table = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                         round256((size_t)batch * l.Hkv * seq_len * l.D * l.esize));
+  a.B = batch;
+  a.T = seq_len;
+  a.Hq = l.Hq;
+  a.Hkv = l.Hkv;
+  a.G = l.G;
+  a.D = l.D;
+  a.sliding = l.sliding;
+  a.window = l.window;
+  a.scale = l.scale;
+  fill_rope(l, &a.rope);
+  hipError_t e = hgqa::launch_prefill(a, l.elem, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kv_append(const hgqa_layer* layer, int32_t batch, int32_t n_new, const int32_t* start_pos,
+              int32_t max_end_pos, const void* k_new, const void* v_new, void* k_cache,
+              void* v_cache, int32_t cache_capacity, void* stream) {
+  Layer l;
+  int rc = check_layer(layer, &l);
+  if (rc != HGQA_OK) return rc;
+  if (batch < 0 || n_new < 0) return fail(HGQA_EINVAL, "batch and n_new must be >= 0");
+  if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
+  if (l.sliding && cache_capacity != l.window)
+    return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
+                l.window, cache_capacity);
+  if (max_end_pos < n_new) return fail(HGQA_EINVAL, "max_end_pos must be >= n_new");
+  if (!l.sliding && max_end_pos > cache_capacity)
+    return fail(HGQA_ENOSPACE, "max_end_pos %d exceeds the full cache capacity %d", max_end_pos,
+                cache_capacity);
+  if (batch == 0 || n_new == 0) return ok();
+  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
+  if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "cache too large");
+  if (!start_pos || !k_new || !v_new || !k_cache || !v_cache)
+    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(HGQA_EINVAL, "k_new, v_new and the caches must be 16-byte aligned");
+  hgqa::AppendArgs a{};
+  a.start_pos = start_pos;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.B = batch;
+  a.n_new = n_new;
+  a.Hkv = l.Hkv;
+  a.D = l.D;
+  a.cap = cache_capacity;
+  a.sliding = l.sliding;
+  a.window = l.window;
+  fill_rope(l, &a.rope);
+  hipError_t e = hgqa::launch_kv_append(a, l.elem, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(HGQA_EHIP, "kv_append launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t max_seq_len,
+                                   int32_t cache_capacity) {
+  Layer l;
+  if (check_layer(layer, &l) != HGQA_OK || batch < 1 || max_seq_len < 1) return 0;
+  (void)cache_capacity;
+  return hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len)
+      .workspace_bytes;
+}
+
+int attn_decode(const hgqa_layer* layer, int32_t batch, const void* q, const void* gate,
+                const void* k_cache, const void* v_cache, int32_t cache_capacity,
+                const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
+                size_t workspace_bytes, void* out, void* stream) {
+  Layer l;
+  int rc = check_layer(layer, &l);
+  if (rc != HGQA_OK) return rc;
+  if (batch < 0) return fail(HGQA_EINVAL, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
+  if (max_seq_len < 1) return fail(HGQA_EINVAL, "max_seq_len must be >= 1");
+  if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
+  if (l.sliding && cache_capacity != l.window)
+    return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
+                l.window, cache_capacity);
+  if (!l.sliding && max_seq_len > cache_capacity)
+    return fail(HGQA_ENOSPACE, "max_seq_len %d exceeds the full cache capacity %d", max_seq_len,
+                cache_capacity);
+  if (l.elem == hgqa::Elem::BF16 && l.G > 16)
+    return fail(HGQA_EUNSUPPORTED, "bf16 decode supports gqa_ratio <= 16 (got %d)", l.G);
+  if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "cache too large");
+  if (!q || !gate || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(HGQA_EINVAL, "q, the caches and out must be 16-byte aligned");
+  if (out == q || out == gate) return fail(HGQA_EINVAL, "out must not alias an input");
+  const hgqa::DecodePlan plan =
+      hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len);
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return fail(HGQA_EINVAL, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HGQA_EINVAL, "workspace must be 16-byte aligned");
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  plan.workspace_bytes);
+  }
+  if ((long long)batch * plan.num_splits * l.Hkv > 0x7fffffffLL)
+    return fail(HGQA_EUNSUPPORTED, "too many decode blocks");
+  hgqa::DecodeArgs a{};
+  a.q = q;
+  a.gate = gate;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.B = batch;
+  a.Hq = l.Hq;
+  a.Hkv = l.Hkv;
+  a.G = l.G;
+  a.D = l.D;
+  a.cap = cache_capacity;
+  a.max_seq_len = max_seq_len;
+  a.sliding = l.sliding;
+  a.window = l.window;
+  a.split_keys = plan.split_keys;
+  a.num_splits = plan.num_splits;
+  a.scale = l.scale;
+  fill_rope(l, &a.rope);
+  hipError_t e = hgqa::launch_decode(a, l.elem, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(HGQA_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

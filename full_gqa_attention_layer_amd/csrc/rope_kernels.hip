@@ -1,0 +1,132 @@
+// RoPE kernels that touch each key once:
+//  * the prefill pre-pass: rotates K into a head-major copy [B,Hkv,T,D] and
+//    writes the (cos, sin) table [T, r/2] that the attention kernel uses to
+//    rotate Q while loading it;
+//  * kv_append: rotates new keys at their absolute positions and scatters
+//    keys and values into the layer's cache, slot p (full layer) or p mod W
+//    (sliding layer ring).
+// RoPE pairs dim i with dim i + r/2 for i < r/2 at frequency theta^(-2i/r);
+// dims >= r are copied; a base of 0 is the identity ("Step-3.7-Flash-oQ3e"
+// walkthrough 2.3; "Muse-Glimmer-30B-6bit" walkthrough, "the RoPE zero value").
+#include "device_util.h"
+
+namespace hgqa {
+
+template <typename T> struct ElemIO;
+template <> struct ElemIO<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+template <> struct ElemIO<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+
+// Rotated value of element d of one head row x[0..D) whose (cos, sin) for
+// pair i sit in cs[i].
+template <typename T>
+__device__ __forceinline__ float rope_elem(const T* x, int d, int half, int rdims,
+                                           const float2* cs) {
+  float xv = ElemIO<T>::load(x + d);
+  if (d < half) {
+    float2 c = cs[d];
+    float y = ElemIO<T>::load(x + d + half);
+    return fmaf(xv, c.x, -y * c.y);
+  }
+  if (d < rdims) {
+    float2 c = cs[d - half];
+    float y = ElemIO<T>::load(x + d - half);
+    return fmaf(xv, c.x, y * c.y);
+  }
+  return xv;
+}
+
+constexpr int kPrepassPositions = 16;
+
+// grid (ceil(T/16), B), block 256.
+template <typename T>
+__global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
+  __shared__ float2 cs[kPrepassPositions][kMaxHalfRotary];
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kPrepassPositions;
+  const int np = min(kPrepassPositions, a.T - t0);
+  const int half = a.rope.half;
+  for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
+    int tp = e / half, i = e - tp * half;
+    float2 c = rope_cos_sin(t0 + tp, a.rope.freq_over_pi[i]);
+    cs[tp][i] = c;
+    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
+  }
+  __syncthreads();
+  const T* k = static_cast<const T*>(a.k);
+  T* kr = static_cast<T*>(a.k_rot);
+  const int D = a.D, Hkv = a.Hkv;
+  const int per_pos = Hkv * D;
+  for (int e = threadIdx.x; e < np * per_pos; e += blockDim.x) {
+    int tp = e / per_pos;
+    int r = e - tp * per_pos;
+    int h = r / D, d = r - h * D;
+    int t = t0 + tp;
+    const T* row = k + (((size_t)b * a.T + t) * Hkv + h) * D;
+    float y = rope_elem<T>(row, d, half, a.rope.rdims, cs[tp]);
+    ElemIO<T>::store(kr + (((size_t)b * Hkv + h) * a.T + t) * D + d, y);
+  }
+}
+
+template <typename T>
+hipError_t launch_prepass_t(const PrefillArgs& a, hipStream_t s) {
+  dim3 grid((a.T + kPrepassPositions - 1) / kPrepassPositions, a.B);
+  hipLaunchKernelGGL(prefill_rope_prepass<T>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s) {
+  return e == Elem::BF16 ? launch_prepass_t<uint16_t>(a, s) : launch_prepass_t<float>(a, s);
+}
+
+// grid (n_new, B), block 256. One block per new token.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  __shared__ float2 cs[kMaxHalfRotary];
+  const int n = blockIdx.x, b = blockIdx.y;
+  const int start = a.start_pos[b];
+  const int p = start + n;
+  if (p < 0) return;
+  int slot;
+  if (a.sliding) {
+    // Only the last W positions of this call reach the ring: each slot keeps
+    // the highest position mapping to it.
+    if (p < start + a.n_new - a.window) return;
+    slot = p % a.window;
+  } else {
+    if (p >= a.cap) return;
+    slot = p;
+  }
+  const int half = a.rope.half;
+  for (int i = threadIdx.x; i < half; i += blockDim.x)
+    cs[i] = rope_cos_sin(p, a.rope.freq_over_pi[i]);
+  __syncthreads();
+  const int D = a.D, Hkv = a.Hkv;
+  const T* kn = static_cast<const T*>(a.k_new) + ((size_t)b * a.n_new + n) * Hkv * D;
+  const T* vn = static_cast<const T*>(a.v_new) + ((size_t)b * a.n_new + n) * Hkv * D;
+  T* kc = static_cast<T*>(a.k_cache);
+  T* vc = static_cast<T*>(a.v_cache);
+  for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+    int h = e / D, d = e - h * D;
+    size_t dst = (((size_t)b * Hkv + h) * a.cap + slot) * D + d;
+    float y = rope_elem<T>(kn + h * D, d, half, a.rope.rdims, cs);
+    ElemIO<T>::store(kc + dst, y);
+    vc[dst] = vn[e];
+  }
+}
+
+hipError_t launch_kv_append(const AppendArgs& a, Elem e, hipStream_t s) {
+  dim3 grid(a.n_new, a.B);
+  if (e == Elem::BF16)
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hgqa

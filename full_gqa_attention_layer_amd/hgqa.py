@@ -1,0 +1,186 @@
+"""Python binding of libhgqa.so: the C ABI of include/hgqa.h under the same names.
+
+This module only marshals arguments: it checks tensor shapes, dtypes and
+devices, allocates outputs and workspaces with torch, and passes raw device
+pointers and the current HIP stream. Every step of the computation runs in
+the library's HIP kernels. If the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhgqa.so")
+
+FULL, SLIDING = 0, 1
+BF16, FP32 = 0, 1
+OK, EINVAL, EUNSUPPORTED, ENOSPACE, EHIP = 0, -1, -2, -3, -4
+
+EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "kv_append",
+            "attn_decode_workspace_bytes", "attn_decode", "hgqa_last_error")
+
+
+class HgqaLayer(ctypes.Structure):
+    """Mirror of the C struct hgqa_layer."""
+    _fields_ = [("layer_type", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("gqa_ratio", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+                ("rotary_fraction", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class HgqaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"hgqa error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libhgqa.so once and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() or "
+                           "python -m full_gqa_attention_layer_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    LP = ctypes.POINTER(HgqaLayer)
+    lib.attn_prefill_workspace_bytes.argtypes = [LP, I, I]
+    lib.attn_prefill_workspace_bytes.restype = S
+    lib.attn_prefill.argtypes = [LP, I, I, P, P, P, P, P, P, S, P]
+    lib.attn_prefill.restype = ctypes.c_int
+    lib.kv_append.argtypes = [LP, I, I, P, I, P, P, P, P, I, P]
+    lib.kv_append.restype = ctypes.c_int
+    lib.attn_decode_workspace_bytes.argtypes = [LP, I, I, I]
+    lib.attn_decode_workspace_bytes.restype = S
+    lib.attn_decode.argtypes = [LP, I, P, P, P, P, I, P, I, P, S, P, P]
+    lib.attn_decode.restype = ctypes.c_int
+    lib.hgqa_last_error.argtypes = []
+    lib.hgqa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def hgqa_last_error() -> str:
+    return load_library().hgqa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise HgqaError(rc, hgqa_last_error())
+
+
+def layer(layer_type: int, window: int, num_q_heads: int, gqa_ratio: int, head_dim: int,
+          rope_theta: float, rotary_fraction: float = 1.0, softmax_scale: float = 0.0,
+          dtype: int = BF16) -> HgqaLayer:
+    return HgqaLayer(layer_type, window, num_q_heads, gqa_ratio, head_dim, rope_theta,
+                     rotary_fraction, softmax_scale, dtype)
+
+
+def layer_from_shape(shape, dtype: int = BF16) -> HgqaLayer:
+    """Descriptor of a workloads.LayerShape."""
+    return layer(shape.layer_type, shape.window, shape.num_q_heads, shape.gqa_ratio,
+                 shape.head_dim, shape.rope_theta, shape.rotary_fraction,
+                 shape.softmax_scale, dtype)
+
+
+def _torch_dtype(L: HgqaLayer):
+    return torch.bfloat16 if L.dtype == BF16 else torch.float32
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def attn_prefill_workspace_bytes(L: HgqaLayer, batch: int, seq_len: int) -> int:
+    return int(load_library().attn_prefill_workspace_bytes(ctypes.byref(L), batch, seq_len))
+
+
+def attn_prefill(L: HgqaLayer, q, k, v, gate, out=None, workspace=None):
+    """Gated causal/sliding GQA of a prompt at positions 0..T-1 (see hgqa.h)."""
+    lib = load_library()
+    B, T, Hq, D = q.shape
+    Hkv = Hq // max(L.gqa_ratio, 1)
+    dt = _torch_dtype(L)
+    _need(q, "q", (B, T, L.num_q_heads, L.head_dim), dt)
+    _need(k, "k", (B, T, Hkv, D), dt)
+    _need(v, "v", (B, T, Hkv, D), dt)
+    _need(gate, "gate", (B, T, Hq), dt)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", (B, T, Hq, D), dt)
+    need = attn_prefill_workspace_bytes(L, B, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_prefill(ctypes.byref(L), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                            _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def kv_append(L: HgqaLayer, start_pos, max_end_pos: int, k_new, v_new, k_cache, v_cache):
+    """Rotate and scatter new K/V into the layer's cache (see hgqa.h)."""
+    lib = load_library()
+    B, n, Hkv, D = k_new.shape
+    cap = k_cache.shape[2]
+    dt = _torch_dtype(L)
+    _need(start_pos, "start_pos", (B,), torch.int32)
+    _need(k_new, "k_new", (B, n, Hkv, D), dt)
+    _need(v_new, "v_new", (B, n, Hkv, D), dt)
+    _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
+    _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    _check(lib.kv_append(ctypes.byref(L), B, n, _ptr(start_pos), int(max_end_pos), _ptr(k_new),
+                         _ptr(v_new), _ptr(k_cache), _ptr(v_cache), cap, _stream()))
+
+
+def attn_decode_workspace_bytes(L: HgqaLayer, batch: int, max_seq_len: int,
+                                cache_capacity: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(ctypes.byref(L), batch, max_seq_len,
+                                                          cache_capacity))
+
+
+def attn_decode(L: HgqaLayer, q, gate, k_cache, v_cache, seq_lens, max_seq_len: int,
+                out=None, workspace=None):
+    """One query token per sequence against its cache (see hgqa.h)."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dt = _torch_dtype(L)
+    _need(q, "q", (B, L.num_q_heads, L.head_dim), dt)
+    _need(gate, "gate", (B, Hq), dt)
+    _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
+    _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", (B, Hq, D), dt)
+    need = attn_decode_workspace_bytes(L, B, max_seq_len, cap)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_decode(ctypes.byref(L), B, _ptr(q), _ptr(gate), _ptr(k_cache),
+                           _ptr(v_cache), cap, _ptr(seq_lens), int(max_seq_len),
+                           _ptr(workspace), ws_bytes, _ptr(out), _stream()))
+    return out

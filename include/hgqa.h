@@ -1,0 +1,177 @@
+/*
+ * hgqa.h - hybrid sliding/full grouped-query attention for MI355X (gfx950).
+ *
+ * The C ABI of libhgqa.so. One attention layer of a hybrid stack in which
+ * most layers attend through a sliding window and one layer in four attends
+ * to the whole causal context:
+ *
+ *   y[b,i,h] = sigmoid(gate[b,i,h]) * sum_j P[i,j] * V[b,j,h/G]
+ *   P[i,:]   = softmax over visible j of scale * <rope(q_i, i), rope(k_j, j)>
+ *   visible  : j <= i, and for a sliding layer also i - j < W
+ *
+ * Sources, cited by page and section:
+ *   "Step-3.7-Flash-oQ3e" walkthrough, section 2: layer_types selects full or
+ *   sliding attention per layer (2.1, 2.2); both masks are built once and each
+ *   layer picks its own (2.2); a sliding layer's cache keeps W = 512 tokens
+ *   (2.2); rope_theta is per layer and full layers rotate only half of
+ *   head_dim (2.3); every head has its own sigmoid gate (2.3).
+ *   "Step-3.7-Flash" model card, table "config.json: all 49 fields": 64 heads
+ *   in 8 KV groups (GQA), head_dim 128, sliding_window 512, sink false.
+ *   "Muse-Glimmer-30B-6bit" walkthrough, sections "GQA 16:1" (32 Q / 2 KV
+ *   heads), "sliding window attention: 39 + 13" (W = 2048, one full layer in
+ *   four), "the RoPE zero value" (base 0 means no rotation), and "each layer:
+ *   double LayerNorm + gated attention" (gate_proj: sigmoid gate on the
+ *   attention output).
+ *
+ * Readings where the pages are silent: W counts keys including the query;
+ * RoPE pairs dim i with dim i + r/2 inside the first r = round(f * D) dims at
+ * frequency theta^(-2i/r); Q head h reads KV head h / G (contiguous groups);
+ * positions are 0-based; one gate logit per (token, head).
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers unless marked [host]. The caller owns every
+ *     buffer. Buffers are dense row-major in the layouts given, 16-byte
+ *     aligned, and outputs do not alias inputs.
+ *   - Arguments are checked on the host before anything is enqueued; an
+ *     invalid call returns a negative HGQA_E* code, enqueues nothing and
+ *     leaves a message for hgqa_last_error().
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the legacy default
+ *     stream) and the call returns without waiting for it.
+ *   - The library allocates no device memory and keeps no state between calls
+ *     besides a per-thread error message. Scratch memory is passed in by the
+ *     caller as `workspace`, sized by the matching *_workspace_bytes query.
+ *   - Device-side integers (start_pos, seq_lens) are trusted within the
+ *     host-side bounds passed with them; values outside are clamped so that
+ *     no access leaves the buffers, and the result for them is unspecified.
+ */
+#ifndef HGQA_H
+#define HGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Layer kinds ("Step-3.7-Flash-oQ3e" walkthrough 2.1: layer_types). */
+enum { HGQA_FULL = 0, HGQA_SLIDING = 1 };
+
+/* Element type of Q, K, V, gate, output and caches (all the same). */
+enum { HGQA_BF16 = 0, HGQA_FP32 = 1 };
+
+/* Return codes. */
+enum {
+  HGQA_OK = 0,
+  HGQA_EINVAL = -1,       /* malformed argument                          */
+  HGQA_EUNSUPPORTED = -2, /* well formed but not implemented (shape/type)  */
+  HGQA_ENOSPACE = -3,     /* workspace or cache too small                  */
+  HGQA_EHIP = -4          /* the HIP runtime reported an error on launch   */
+};
+
+/*
+ * One layer's attention settings, as the model config gives them.
+ *   layer_type      HGQA_FULL or HGQA_SLIDING
+ *   window          W >= 1 keys visible to a query, itself included
+ *                   (sliding only; ignored for full layers)
+ *   num_q_heads     Hq >= 1
+ *   gqa_ratio       G >= 1 query heads per KV head; Hkv = Hq / G, Hq % G == 0
+ *   head_dim        D: 64 or 128
+ *   rope_theta      RoPE base >= 0; 0 means no rotation
+ *   rotary_fraction f in [0, 1]; r = round(f * D) leading dims rotate.
+ *                   r must be even; bf16 layers need r % 16 == 0.
+ *                   r == 0 means no rotation.
+ *   softmax_scale   > 0 to set the scale; <= 0 selects 1 / sqrt(D)
+ *   dtype           HGQA_BF16 or HGQA_FP32
+ */
+typedef struct {
+  int32_t layer_type;
+  int32_t window;
+  int32_t num_q_heads;
+  int32_t gqa_ratio;
+  int32_t head_dim;
+  float rope_theta;
+  float rotary_fraction;
+  float softmax_scale;
+  int32_t dtype;
+} hgqa_layer;
+
+/*
+ * Scratch bytes attn_prefill needs for this layer and shape: the rotated K,
+ * [B, Hkv, T, D] in the layer dtype, and a cos/sin table [T, r/2] of float
+ * pairs, each part rounded up to 256 bytes. Returns 0 for an invalid layer.
+ */
+size_t attn_prefill_workspace_bytes(const hgqa_layer* layer, int32_t batch,
+                                    int32_t seq_len);
+
+/*
+ * Prefill: attention of a whole prompt at positions 0..T-1 over itself.
+ *   q     [B, T, Hq, D]   queries, not rotated
+ *   k, v  [B, T, Hkv, D]  keys (not rotated) and values
+ *   gate  [B, T, Hq]      gate logits
+ *   out   [B, T, Hq, D]   gated attention output
+ *   workspace            >= attn_prefill_workspace_bytes(layer, B, T) bytes
+ * batch == 0 or seq_len == 0 is a valid call that does nothing.
+ * The masks follow "Step-3.7-Flash-oQ3e" walkthrough 2.2; RoPE and the gate
+ * follow 2.3 of the same page.
+ */
+int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len,
+                 const void* q, const void* k, const void* v, const void* gate,
+                 void* out, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Append new tokens to a layer's KV cache.
+ *   start_pos    [B] int32  absolute position of k_new[b, 0]; >= 0
+ *   max_end_pos  [host]     >= start_pos[b] + n_new for every b
+ *   k_new, v_new [B, n_new, Hkv, D]  new keys (not rotated) and values
+ *   k_cache, v_cache [B, Hkv, cache_capacity, D]
+ * Token n of sequence b sits at p = start_pos[b] + n. Its key, rotated at p,
+ * and its value are written to slot p of a full layer's cache (which needs
+ * cache_capacity >= max_end_pos), or to slot p mod W of a sliding layer's
+ * ring, whose cache_capacity must equal W ("Step-3.7-Flash-oQ3e" walkthrough
+ * 2.2: a sliding layer's cache keeps only W tokens). When one call writes
+ * more than W tokens to a ring, only the last W positions are written, so
+ * each slot ends with the highest position that maps to it.
+ */
+int kv_append(const hgqa_layer* layer, int32_t batch, int32_t n_new,
+              const int32_t* start_pos, int32_t max_end_pos,
+              const void* k_new, const void* v_new, void* k_cache,
+              void* v_cache, int32_t cache_capacity, void* stream);
+
+/*
+ * Scratch bytes attn_decode needs: per-split partial results (running max,
+ * running sum and unnormalised output, float32) for the split count the
+ * library picks for this shape. May be 0 when no split is needed.
+ */
+size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch,
+                                   int32_t max_seq_len, int32_t cache_capacity);
+
+/*
+ * Decode: one new query token per sequence against its cache.
+ *   q        [B, Hq, D]  queries, not rotated; the query of sequence b sits
+ *                        at position seq_lens[b] - 1
+ *   gate     [B, Hq]     gate logits
+ *   k_cache, v_cache [B, Hkv, cache_capacity, D] as written by kv_append
+ *                        (K rotated), already holding the new token
+ *   seq_lens [B] int32   tokens in the cache including the new one, >= 1
+ *   max_seq_len [host]   >= every seq_lens[b]; full layers need
+ *                        cache_capacity >= max_seq_len
+ *   out      [B, Hq, D]
+ * A full layer attends to slots 0..L-1; a sliding layer's ring holds the
+ * last min(L, W) positions and the query attends to all of them.
+ */
+int attn_decode(const hgqa_layer* layer, int32_t batch, const void* q,
+                const void* gate, const void* k_cache, const void* v_cache,
+                int32_t cache_capacity, const int32_t* seq_lens,
+                int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                void* out, void* stream);
+
+/* Text of the last error returned on the calling thread ("" if none). */
+const char* hgqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGQA_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports what include/hgqa.h declares, and rejects
+invalid calls on the host before touching the GPU (no device needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from full_gqa_attention_layer_amd import hgqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hgqa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hgqa.LIB_PATH):
+        from full_gqa_attention_layer_amd import build
+        build.build()
+    return hgqa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    assert names == sorted(hgqa.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(hgqa.HgqaLayer) == 36
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} hgqa_layer;", text, flags=re.S).group(1)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [f for _, f in fields] == [f for f, _ in hgqa.HgqaLayer._fields_]
+
+
+def _call_prefill(lib, L, B=1, T=16, ws=1 << 20, ptr=16):
+    p = ctypes.c_void_p(ptr)
+    return lib.attn_prefill(ctypes.byref(L), B, T, p, p, p, p, ctypes.c_void_p(ptr + 4096), p,
+                            ws, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layer_type=2), hgqa.EINVAL),
+    (dict(window=0), hgqa.EINVAL),
+    (dict(num_q_heads=0), hgqa.EINVAL),
+    (dict(gqa_ratio=0), hgqa.EINVAL),
+    (dict(num_q_heads=12, gqa_ratio=5), hgqa.EINVAL),
+    (dict(head_dim=96), hgqa.EUNSUPPORTED),
+    (dict(rope_theta=-1.0), hgqa.EINVAL),
+    (dict(rope_theta=float("nan")), hgqa.EINVAL),
+    (dict(rotary_fraction=1.5), hgqa.EINVAL),
+    (dict(rotary_fraction=3.0 / 128), hgqa.EINVAL),            # r = 3, odd
+    (dict(rotary_fraction=8.0 / 128), hgqa.EUNSUPPORTED),      # bf16 needs r % 16 == 0
+    (dict(softmax_scale=float("inf")), hgqa.EINVAL),
+    (dict(dtype=7), hgqa.EINVAL),
+])
+def test_invalid_descriptors_are_rejected(lib, kw, code):
+    args = dict(layer_type=1, window=64, num_q_heads=8, gqa_ratio=4, head_dim=128,
+                rope_theta=1e4, rotary_fraction=1.0, softmax_scale=0.0, dtype=hgqa.BF16)
+    args.update(kw)
+    L = hgqa.HgqaLayer(**args)
+    assert _call_prefill(lib, L) == code
+    assert hgqa.hgqa_last_error() != ""
+
+
+def test_prefill_argument_checks(lib):
+    L = hgqa.layer(1, 64, 8, 4, 128, 1e4)
+    assert _call_prefill(lib, L, B=-1) == hgqa.EINVAL
+    assert _call_prefill(lib, L, B=0) == hgqa.OK          # empty batch: nothing to do
+    assert _call_prefill(lib, L, T=0) == hgqa.OK
+    assert _call_prefill(lib, L, ptr=8) == hgqa.EINVAL    # misaligned
+    need = lib.attn_prefill_workspace_bytes(ctypes.byref(L), 1, 16)
+    assert need > 0
+    assert _call_prefill(lib, L, ws=need - 1) == hgqa.ENOSPACE
+    z = ctypes.c_void_p(0)
+    assert lib.attn_prefill(ctypes.byref(L), 1, 16, z, z, z, z, z, z, 1 << 20, None) == hgqa.EINVAL
+    assert lib.attn_prefill(None, 1, 16, z, z, z, z, z, z, 0, None) == hgqa.EINVAL
+
+
+def test_prefill_workspace_formula(lib):
+    L = hgqa.layer(1, 512, 96, 12, 128, 1e4)
+    # rotated K [B,Hkv,T,D] bf16 + cos/sin table [T, r/2] float pairs
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(L), 1, 8192) == 8192 * 8 * 128 * 2 + 8192 * 64 * 8
+    Lf = hgqa.layer(0, 0, 4, 4, 64, 1e4, 1.0, 0.0, hgqa.FP32)
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 1, 256) == 256 * 64 * 4 + 256 * 32 * 8
+
+
+def test_kv_append_argument_checks(lib):
+    p = ctypes.c_void_p(256)
+    Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
+    # ring capacity must equal W
+    assert lib.kv_append(ctypes.byref(Ls), 1, 1, p, 10, p, p, p, p, 256, None) == hgqa.EINVAL
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    assert lib.kv_append(ctypes.byref(Lf), 1, 1, p, 101, p, p, p, p, 100, None) == hgqa.ENOSPACE
+    assert lib.kv_append(ctypes.byref(Lf), 1, 4, p, 3, p, p, p, p, 100, None) == hgqa.EINVAL
+    assert lib.kv_append(ctypes.byref(Lf), 1, 0, p, 3, p, p, p, p, 100, None) == hgqa.OK
+    z = ctypes.c_void_p(0)
+    assert lib.kv_append(ctypes.byref(Lf), 1, 1, z, 3, p, p, p, p, 100, None) == hgqa.EINVAL
+
+
+def test_decode_argument_checks(lib):
+    p = ctypes.c_void_p(256)
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    ws = lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072, 131072)
+    assert ws > 0
+    o = ctypes.c_void_p(4096)
+    args = lambda cap, mx, wsb: (ctypes.byref(Lf), 64, p, p, p, p, cap, p, mx, p, wsb, o, None)
+    assert lib.attn_decode(*args(100, 101, ws)) == hgqa.ENOSPACE
+    assert lib.attn_decode(*args(131072, 131072, ws - 1)) == hgqa.ENOSPACE
+    assert lib.attn_decode(*args(131072, 0, ws)) == hgqa.EINVAL
+    assert lib.attn_decode(ctypes.byref(Lf), 64, p, p, p, p, 131072, p, 131072, p, ws, p,
+                           None) == hgqa.EINVAL                  # out aliases q
+    Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
+    assert lib.attn_decode(ctypes.byref(Ls), 1, p, p, p, p, 100, p, 10, p, 1 << 20, p,
+                           None) == hgqa.EINVAL
+    Lg = hgqa.layer(0, 0, 64, 2, 128, 5e6, 0.5)
+    Lg.gqa_ratio = 32
+    assert lib.attn_decode(ctypes.byref(Lg), 1, p, p, p, p, 100, p, 10, p, 1 << 20, p,
+                           None) == hgqa.EUNSUPPORTED
