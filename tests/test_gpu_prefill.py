@@ -65,14 +65,31 @@ def test_prefill_small_shapes_all_rows(idx):
 
 
 def test_peaky_scores():
-    """Queries scaled by 8 make the softmax nearly one-hot."""
+    """Queries scaled by 8 make the softmax nearly one-hot and the scores 8x
+    larger, so the bf16 rounding of the rotated q and k (the MFMA inputs)
+    moves the scores 8x further than at unit scale. Two checks:
+      * against the oracle fed the same rounded rotated q and k (base 0 on
+        pre-rotated inputs): the usual bf16 bar, which isolates everything
+        else the kernel does;
+      * against the plain oracle: max-abs within 8 x the usual bar (the score
+        error, and with it the output error, grows linearly with q's scale),
+        mean-abs within the usual bar."""
     require_gpu()
+    s = 8
     shape = LayerShape(SLIDING, 64, 16, 2, 128, 1e4, 1.0)
     q, k, v, g = prefill_inputs(shape, 1, 400, hgqa.BF16, (0, 150, 0))
-    q = (q.float() * 8).to(torch.bfloat16)
+    q = (q.float() * s).to(torch.bfloat16)
     out = run_prefill(shape, hgqa.BF16, q, k, v, g)
+    pos = np.arange(400, dtype=np.float64)[None, :, None]
+    qr = oracle.round_bf16(oracle.rope(f64(q), pos, 1e4, 128))
+    kr = oracle.round_bf16(oracle.rope(f64(k), pos, 1e4, 128))
+    unrotated = LayerShape(SLIDING, 64, 16, 2, 128, 0.0, 1.0)
+    ref_r = oracle.prefill(qr, kr, f64(v), f64(g), spec(unrotated))
+    assert_close(out, ref_r, hgqa.BF16, "peaky vs rounded rotated inputs")
     ref = oracle.prefill(f64(q), f64(k), f64(v), f64(g), spec(shape))
-    assert_close(out, ref, hgqa.BF16, "peaky")
+    err = np.abs(f64(out) - ref)
+    print(f"peaky vs exact: max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
+    assert err.max() <= s * 2e-2 and err.mean() <= 2e-3
 
 
 class Rows:
