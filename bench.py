@@ -14,7 +14,7 @@ same prefill (whole KV groups of the layer) and reported under
 "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
-                    [--no-cpu-baseline] [--only prefill|decode]
+                    [--no-cpu-baseline] [--only prefill|decode|copy]
 """
 from __future__ import annotations
 
@@ -39,7 +39,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None)
+    p.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                   help="copy: a plain 1 GiB device copy, the reference kernel for "
+                        "scaling HBM byte counters")
     p.add_argument("--cpu-groups", type=int, default=8,
                    help="KV groups of the layer in the CPU-oracle sample")
     return p.parse_args()
@@ -177,6 +179,8 @@ def bench_decode(args, torch, hgqa, synth, workloads, acc):
                 synth.device_normal_(kc[b], (0, wl.wid, li, synth.CACHE_K, b, s))
                 synth.device_normal_(vc[b], (0, wl.wid, li, synth.CACHE_V, b, s))
             caches.append((kc, vc))
+        print(f"[bench] decode layer {li}: {nsets} cache set(s) filled", file=sys.stderr,
+              flush=True)
         key = (0, wl.wid, li)
         q = synth.host_normal((B, Hq, D), key + (synth.Q,)).to(dev)
         g = synth.host_normal((B, Hq), key + (synth.GATE,)).to(dev)
@@ -268,6 +272,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
     hgqa.load_library()
     rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -38,18 +38,22 @@ def device_seed(key) -> int:
     return ((int(a) << 32) | int(b)) & ((1 << 63) - 1)
 
 
+DEVICE_CHUNK = 1 << 28  # elements drawn per generator call
+
+
 def device_normal_(out: torch.Tensor, key) -> torch.Tensor:
-    """Fill a device tensor in place with standard normals from torch's Philox
-    generator, drawn in float32 and rounded to out.dtype. Large tensors are
-    filled in slices along dim 0, each slice keyed by (key..., slice index)."""
-    assert out.is_cuda
-    for i in range(out.shape[0]):
+    """Fill a contiguous device tensor in place with standard normals from
+    torch's Philox generator, drawn in float32 and rounded to out.dtype. The
+    flattened tensor is drawn in chunks of DEVICE_CHUNK elements, chunk i
+    keyed by (key..., i)."""
+    assert out.is_cuda and out.is_contiguous()
+    flat = out.view(-1)
+    for i, lo in enumerate(range(0, flat.numel(), DEVICE_CHUNK)):
+        hi = min(flat.numel(), lo + DEVICE_CHUNK)
         g = torch.Generator(device=out.device)
         g.manual_seed(device_seed(tuple(key) + (i,)))
-        tmp = torch.randn(out[i].shape, generator=g, device=out.device,
-                          dtype=torch.float32)
-        out[i].copy_(tmp)
-        del tmp
+        flat[lo:hi].copy_(torch.randn(hi - lo, generator=g, device=out.device,
+                                      dtype=torch.float32))
     return out
 
 
