@@ -33,34 +33,45 @@ constexpr int kRows = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kBN = 64;                       // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
-struct PrefillLds {
-  static constexpr int KSTR = D + 8;    // bf16 per K row (pad: conflict-free b128 reads)
-  static constexpr int VSTR = kBN + 8;  // bf16 per V^T row
-  uint16_t k[2][kBN * KSTR];
-  uint16_t vt[2][D * VSTR];
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// K and V tiles sit in LDS as [64 keys][D] bf16 rows, unpadded. The 16-byte
+// chunk c of key row k is stored at chunk position c ^ swz(k); the global
+// loads pick their source chunk so that each lane's 16 bytes land at its own
+// position (global_load_lds writes lane l at base + 16 l). The swizzles make
+// both readers conflict-free:
+//  * K: ds_read_b128, 16 lanes read one chunk of 16 consecutive keys;
+//  * V: ds_read_b64_tr_b16, 32 lanes read 4 consecutive keys x 4 chunks.
+template <int D> struct Swz;
+template <> struct Swz<128> {  // 64-dword rows: only the chunk position moves banks
+  static __device__ __forceinline__ int k(int key) { return key & 15; }
+  static __device__ __forceinline__ int v(int key) { return 4 * (key & 3); }
+};
+template <> struct Swz<64> {   // 32-dword rows: odd rows sit 32 banks over
+  static __device__ __forceinline__ int k(int key) { return (key >> 1) & 7; }
+  static __device__ __forceinline__ int v(int key) { return 4 * ((key >> 1) & 1); }
 };
 
-// Column of key k (0..63) of a tile inside a V^T row. Within each group of 16
-// keys, the 8 keys one lane half feeds to one 32x32x16 product are adjacent.
-__device__ __forceinline__ int vt_col(int k) {
-  int kk = k & 15;
-  return (k & ~15) + 8 * ((kk >> 2) & 1) + 4 * (kk >> 3) + (kk & 3);
-}
+template <int D>
+struct PrefillLds {
+  uint16_t k[2][kBN * D];
+  uint16_t v[2][kBN * D];
+};
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  constexpr int KCH = D / 8;                  // 16-byte chunks per row
-  constexpr int KLOADS = kBN * KCH / 256;     // K chunks per thread per tile
-  constexpr int VITEMS = (kBN / 4) * KCH;     // (key quad, chunk) items per tile
-  constexpr int KSTR = PrefillLds<D>::KSTR;
-  constexpr int VSTR = PrefillLds<D>::VSTR;
+  constexpr int CH = D / 8;                   // 16-byte chunks per row
+  constexpr int PER_WAVE = CH / 4;            // 1 KB loads per wave per operand per tile
   constexpr int NS = D / 16;                  // k-steps of the score product
   constexpr int NDB = D / 32;                 // 32-wide d blocks of the output
   __shared__ PrefillLds<D> sm;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int n = lane & 31, g = lane >> 5;
   const int T = a.T, G = a.G, Hq = a.Hq, Hkv = a.Hkv;
   const int TG = T * G;
@@ -136,47 +147,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const uint16_t* vbase = vp + ((size_t)b * T * Hkv + kvh) * D;
   const size_t vstride = (size_t)Hkv * D;
 
-  u32x4_t kreg[KLOADS];
-  u32x4_t vreg[4];
-  const int vq = tid / KCH, vdc = tid - (tid / KCH) * KCH;
-
-  auto load_tile = [&](int j0) {
+  // HBM -> LDS without registers: each wave moves PER_WAVE 1 KB pieces of
+  // both tiles. Keys past the end re-read the last key: finite values that
+  // the causal mask hides (their probabilities are exactly 0).
+  auto load_tile = [&](int j0, int st) {
 #pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int c = tid + 256 * u;
-      const int key = c / KCH, dc = c - key * KCH;
-      const int j = j0 + key;
-      kreg[u] = (j < T) ? *reinterpret_cast<const u32x4_t*>(kbase + (size_t)j * D + dc * 8)
-                        : u32x4_t{0, 0, 0, 0};
-    }
-    if (tid < VITEMS) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int j = j0 + 4 * vq + kk;
-        vreg[kk] = (j < T) ? *reinterpret_cast<const u32x4_t*>(vbase + (size_t)j * vstride + vdc * 8)
-                           : u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int st) {
-#pragma unroll
-    for (int u = 0; u < KLOADS; ++u) {
-      const int c = tid + 256 * u;
-      const int key = c / KCH, dc = c - key * KCH;
-      *reinterpret_cast<u32x4_t*>(&sm.k[st][key * KSTR + dc * 8]) = kreg[u];
-    }
-    if (tid < VITEMS) {
-      const int col = vt_col(4 * vq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // dims 2e and 2e+1 of the chunk, for the 4 keys of the quad
-        const uint32_t k0 = vreg[0][e], k1 = vreg[1][e], k2 = vreg[2][e], k3 = vreg[3][e];
-        u32x2_t lo = {(k0 & 0xffffu) | (k1 << 16), (k2 & 0xffffu) | (k3 << 16)};
-        u32x2_t hi = {(k0 >> 16) | (k1 & 0xffff0000u), (k2 >> 16) | (k3 & 0xffff0000u)};
-        const int d = vdc * 8 + 2 * e;
-        *reinterpret_cast<u32x2_t*>(&sm.vt[st][d * VSTR + col]) = lo;
-        *reinterpret_cast<u32x2_t*>(&sm.vt[st][(d + 1) * VSTR + col]) = hi;
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int I = wave * PER_WAVE + i;
+      const int P = 64 * I + lane;
+      const int key = P / CH, pos = P % CH;
+      const int j = min(j0 + key, T - 1);
+      const uint16_t* ksrc = kbase + (size_t)j * D + 8 * (pos ^ Swz<D>::k(key));
+      const uint16_t* vsrc = vbase + (size_t)j * vstride + 8 * (pos ^ Swz<D>::v(key));
+      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.k[st][512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.v[st][512 * I], 16, 0, 0);
     }
   };
 
@@ -185,27 +169,36 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   for (int i = 0; i < NDB; ++i) O[i] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.0f;
   const float sc = a.scale * kLog2e;
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (ntiles > 0) {
-    load_tile(j_lo);
-    store_tile(0);
-  }
+  // V^T operand supplier addresses for ds_read_b64_tr_b16: lane r of each
+  // 16-lane group points at key (4g + r/4) and dims 4(r%4).. of its d half.
+  const int r16 = lane & 15;
+  const int dhalf = (lane >> 4) & 1;
+  const int vkey0 = 4 * g + (r16 >> 2);
+  const int vd = 16 * dhalf + 4 * (r16 & 3);
+
+  if (ntiles > 0) load_tile(j_lo, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
     const int j0 = j_lo + it * kBN;
-    if (it + 1 < ntiles) load_tile(j0 + kBN);
+    if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
+    const uint16_t* ks = sm.k[st];
+    const uint16_t* vs = sm.v[st];
 
     // S^T for two 32-key blocks
     f32x16_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       S[kb] = f32x16_t{};
+      const int key = 32 * kb + n;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(
-            &sm.k[st][(32 * kb + n) * KSTR + 16 * s + 8 * g]);
+        const int pos = (2 * s + g) ^ Swz<D>::k(key);
+        bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + key * D + 8 * pos);
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], S[kb], 0, 0, 0);
       }
     }
@@ -214,13 +207,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     const bool need_mask = (j0 + kBN - 1 > tw_lo) ||
                            (a.sliding && j0 < tw_hi - a.window + 1);
     if (need_mask) {
+      // key j = j0 + 4g + off is visible iff 0 <= t_row - j < W (W = 2^31 when
+      // full): one unsigned compare per element against a per-lane base.
+      const int base = t_row - j0 - 4 * g;
+      const unsigned wlim = a.sliding ? (unsigned)a.window : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int j = j0 + 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
-          const bool vis = (j <= t_row) && (!a.sliding || t_row - j < a.window);
-          if (!vis) S[kb][v] = -INFINITY;
+          const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
+          S[kb][v] = ((unsigned)(base - off) < wlim) ? S[kb][v] : -INFINITY;
         }
     }
 
@@ -231,40 +227,52 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx * sc);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // Rescale the running output only when some row's maximum grew.
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+    }
     m_run = m_new;
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
 
-    float psum = 0.0f;
+    // P = exp2(S*sc - m), packed to bf16 in the B-operand order of PV; the
+    // row sum is taken over the same rounded values.
+    u32x4_t pk[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int ks4 = 0; ks4 < 4; ++ks4) {
+      const int kb = ks4 >> 1, hh = ks4 & 1;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][v], sc, -m_use));
-        S[kb][v] = p;
-        psum += p;
-      }
-    l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-    for (int i = 0; i < NDB; ++i) O[i] *= alpha;
-
-    // O^T += V^T P^T, 4 k-steps of 16 keys
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kb = ks >> 1, hh = ks & 1;
-      u32x4_t pk;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(S[kb][8 * hh + 2 * e], S[kb][8 * hh + 2 * e + 1]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(
-            &sm.vt[st][(32 * db + n) * VSTR + 16 * ks + 8 * g]);
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, O[db], 0, 0, 0);
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e], sc, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e + 1], sc, -m_use));
+        const bf16x2_t pv = {(__bf16)p0, (__bf16)p1};
+        pk[ks4][e] = __builtin_bit_cast(uint32_t, pv);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pv, ones, l_run, false);
       }
     }
 
-    if (it + 1 < ntiles) store_tile(st ^ 1);
+    // O^T += V^T P^T, 4 k-steps of 16 keys; V^T comes transposed out of LDS.
+#pragma unroll
+    for (int ks4 = 0; ks4 < 4; ++ks4) {
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk[ks4]);
+      const int k0 = 16 * ks4 + vkey0, k1 = k0 + 8;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = 32 * db + vd;
+        const int c = d >> 3, hw = d & 7;
+        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(vs + k0 * D + 8 * (c ^ Swz<D>::v(k0)) + hw));
+        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_t*)(vs + k1 * D + 8 * (c ^ Swz<D>::v(k1)) + hw));
+        const i16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va), pb,
+                                                         O[db], 0, 0, 0);
+      }
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
     __syncthreads();
   }
 

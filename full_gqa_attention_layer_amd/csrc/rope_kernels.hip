@@ -41,9 +41,9 @@ __device__ __forceinline__ float rope_elem(const T* x, int d, int half, int rdim
   return xv;
 }
 
-constexpr int kPrepassPositions = 16;
+constexpr int kPrepassPositions = 8;
 
-// grid (ceil(T/16), B), block 256.
+// grid (ceil(T / kPrepassPositions), B), block 256.
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
   __shared__ float2 cs[kPrepassPositions][kMaxHalfRotary];
@@ -73,15 +73,60 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
   }
 }
 
-template <typename T>
-hipError_t launch_prepass_t(const PrefillArgs& a, hipStream_t s) {
-  dim3 grid((a.T + kPrepassPositions - 1) / kPrepassPositions, a.B);
-  hipLaunchKernelGGL(prefill_rope_prepass<T>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+// bf16 variant: 16-byte chunks (r is a multiple of 16, so a chunk never
+// straddles r/2 or r and its RoPE partner is a whole chunk too).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) {
+  constexpr int CH = D / 8;
+  __shared__ float2 cs[kPrepassPositions][kMaxHalfRotary];
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * kPrepassPositions;
+  const int np = min(kPrepassPositions, a.T - t0);
+  const int half = a.rope.half, rdims = a.rope.rdims;
+  for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
+    int tp = e / half, i = e - tp * half;
+    float2 c = rope_cos_sin(t0 + tp, a.rope.freq_over_pi[i]);
+    cs[tp][i] = c;
+    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
+  }
+  __syncthreads();
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  uint16_t* kr = static_cast<uint16_t*>(a.k_rot);
+  const int Hkv = a.Hkv;
+  const int per_pos = Hkv * CH;
+  for (int e = threadIdx.x; e < np * per_pos; e += blockDim.x) {
+    const int tp = e / per_pos;
+    const int r = e - tp * per_pos;
+    const int h = r / CH, d0 = (r - h * CH) * 8;
+    const int t = t0 + tp;
+    const uint16_t* row = k + (((size_t)b * a.T + t) * Hkv + h) * D;
+    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(row + d0);
+    if (d0 < rdims) {
+      const bool first = d0 < half;
+      const int i0 = first ? d0 : d0 - half;
+      const float sgn = first ? -1.0f : 1.0f;
+      u32x4_t praw = *reinterpret_cast<const u32x4_t*>(row + (first ? d0 + half : d0 - half));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float2 c0 = cs[tp][i0 + 2 * q], c1 = cs[tp][i0 + 2 * q + 1];
+        const float y0 = fmaf(bf16_lo(raw[q]), c0.x, sgn * bf16_lo(praw[q]) * c0.y);
+        const float y1 = fmaf(bf16_hi(raw[q]), c1.x, sgn * bf16_hi(praw[q]) * c1.y);
+        raw[q] = pack_bf16x2(y0, y1);
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(kr + (((size_t)b * Hkv + h) * a.T + t) * D + d0) = raw;
+  }
 }
 
 hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s) {
-  return e == Elem::BF16 ? launch_prepass_t<uint16_t>(a, s) : launch_prepass_t<float>(a, s);
+  dim3 grid((a.T + kPrepassPositions - 1) / kPrepassPositions, a.B);
+  if (e == Elem::F32)
+    hipLaunchKernelGGL(prefill_rope_prepass<float>, grid, dim3(256), 0, s, a);
+  else if (a.D == 128)
+    hipLaunchKernelGGL(prefill_rope_prepass_bf16<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(prefill_rope_prepass_bf16<64>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 // grid (n_new, B), block 256. One block per new token.

@@ -12,7 +12,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhgqa.so")
+# HGQA_LIBRARY may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("HGQA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libhgqa.so")
 
 FULL, SLIDING = 0, 1
 BF16, FP32 = 0, 1
