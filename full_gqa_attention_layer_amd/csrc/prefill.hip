@@ -55,6 +55,53 @@ template <> struct Swz<64> {   // 32-dword rows: odd rows sit 32 banks over
   static __device__ __forceinline__ int v(int key) { return 4 * ((key >> 1) & 1); }
 };
 
+__device__ __forceinline__ void unpack8(u32x4_t raw, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_lo(raw[e]);
+    x[2 * e + 1] = bf16_hi(raw[e]);
+  }
+}
+__device__ __forceinline__ bf16x8_t pack8(const float (&x)[8]) {
+  u32x4_t packed;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+  return __builtin_bit_cast(bf16x8_t, packed);
+}
+// x_e <- x_e cos_e + sgn * partner_e sin_e for the 8 pairs whose (cos, sin)
+// start at cs.
+__device__ __forceinline__ void rotate8(float (&x)[8], u32x4_t praw, const float2* cs, float sgn) {
+  const float4* c4 = reinterpret_cast<const float4*>(cs);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 cc = c4[e];  // (cos, sin) of two consecutive pairs
+    x[2 * e] = fmaf(x[2 * e], cc.x, sgn * bf16_lo(praw[e]) * cc.y);
+    x[2 * e + 1] = fmaf(x[2 * e + 1], cc.z, sgn * bf16_hi(praw[e]) * cc.w);
+  }
+}
+
+// Rotates a lane's Q chunks (chunk s = dims 16s+8g..+7) when r/2 = 16 H16:
+// chunk s < H16 pairs with chunk s + H16 of the same lane; chunks up to
+// 2 H16 rotate, the rest pass through.
+template <int NS, int H16>
+__device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t (&qf)[NS], int g,
+                                              const float2* cs) {
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float x[8];
+    unpack8(raw[s], x);
+    if constexpr (H16 > 0) {
+      if (s < 2 * H16) {
+        const bool first = s < H16;
+        const int sp = first ? s + H16 : s - H16;
+        const int i0 = 16 * (first ? s : s - H16) + 8 * g;
+        rotate8(x, raw[sp < NS ? sp : 0], cs + i0, first ? -1.0f : 1.0f);
+      }
+    }
+    qf[s] = pack8(x);
+  }
+}
+
 template <int D>
 struct PrefillLds {
   uint16_t k[2][kBN * D];
@@ -62,9 +109,10 @@ struct PrefillLds {
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CH = D / 8;                   // 16-byte chunks per row
-  constexpr int PER_WAVE = CH / 4;            // 1 KB loads per wave per operand per tile
+  constexpr int PER_WAVE = CH / kWaves;       // 1 KB loads per wave per operand per tile
+  static_assert(CH % kWaves == 0, "each wave moves whole 1 KB pieces");
   constexpr int NS = D / 16;                  // k-steps of the score product
   constexpr int NDB = D / 32;                 // 32-wide d blocks of the output
   __shared__ PrefillLds<D> sm;
@@ -102,43 +150,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const uint16_t* __restrict__ kr = static_cast<const uint16_t*>(a.k_rot);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
 
-  // ---- Q^T fragments, rotated on load: lane holds row n, dims 16s+8g..+7.
-  bf16x8_t qf[NS];
-  {
-    const uint16_t* qrow = qp + ((size_t)(b * T + t_row) * Hq + h) * D;
-    const int half = a.rope.half, rdims = a.rope.rdims;
-    const float2* csrow = a.cs_table + (size_t)t_row * half;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int d0 = 16 * s + 8 * g;
-      u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_lo(raw[e]);
-        x[2 * e + 1] = bf16_hi(raw[e]);
-      }
-      if (d0 < rdims) {
-        const bool first = d0 < half;
-        const int i0 = first ? d0 : d0 - half;
-        const float sgn = first ? -1.0f : 1.0f;
-        u32x4_t praw = *reinterpret_cast<const u32x4_t*>(qrow + (first ? d0 + half : d0 - half));
-        const float4* c4 = reinterpret_cast<const float4*>(csrow + i0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float4 cc = c4[e];  // (cos, sin) of pairs i0+2e, i0+2e+1
-          float p0 = bf16_lo(praw[e]), p1 = bf16_hi(praw[e]);
-          x[2 * e] = fmaf(x[2 * e], cc.x, sgn * p0 * cc.y);
-          x[2 * e + 1] = fmaf(x[2 * e + 1], cc.z, sgn * p1 * cc.w);
-        }
-      }
-      u32x4_t packed;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) packed[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
-      qf[s] = __builtin_bit_cast(bf16x8_t, packed);
-    }
-  }
-
   // ---- key range of the workgroup
   const int j_lo = a.sliding ? max(0, t_lo - a.window + 1) : 0;
   const int ntiles = (t_hi + 1 - j_lo + kBN - 1) / kBN;
@@ -164,6 +175,74 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
+  // The first K/V tile starts moving before anything else.
+  if (ntiles > 0) load_tile(j_lo, 0);
+
+  // ---- cos/sin rows of the workgroup's positions go to LDS (the second K
+  // buffer is idle until the loop starts) when they fit; else Q reads them
+  // from the global table.
+  const int half = a.rope.half, rdims = a.rope.rdims;
+  const int cs_bytes = (t_hi - t_lo + 1) * half * 8;
+  const bool cs_lds = half > 0 && cs_bytes <= (int)sizeof(sm.k[1]);
+  if (cs_lds) {
+    const char* src0 = reinterpret_cast<const char*>(a.cs_table + (size_t)t_lo * half);
+    const int nblk = (cs_bytes + 1023) / 1024;
+    for (int I = wave; I < nblk; I += kWaves) {
+      const int off = min(1024 * I + 16 * lane, cs_bytes - 16);
+      __builtin_amdgcn_global_load_lds((const void*)(src0 + off),
+                                       (lds_void_t*)(reinterpret_cast<char*>(sm.k[1]) + 1024 * I),
+                                       16, 0, 0);
+    }
+  }
+
+  // ---- Q^T fragments: lane holds row n, dims 16s+8g..+7, rotated below.
+  const uint16_t* qrow = qp + ((size_t)(b * T + t_row) * Hq + h) * D;
+  u32x4_t qraw[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qraw[s] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * s + 8 * g);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // tile 0 and the cos/sin rows have landed
+
+  bf16x8_t qf[NS];
+  if (half == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qraw[s]);
+  } else if (half % 16 == 0) {
+    // The RoPE partner of every chunk sits in this lane, half/16 chunks away.
+    const int tl = t_row - t_lo;
+    const float2* csl = reinterpret_cast<const float2*>(sm.k[1]) + tl * half;
+    const float2* csg = a.cs_table + (size_t)t_row * half;
+    switch (half / 16) {
+#define HGQA_ROPE_CASE(H)                                 \
+  case H:                                                 \
+    if (cs_lds) rope_q_inlane<NS, H>(qraw, qf, g, csl);   \
+    else rope_q_inlane<NS, H>(qraw, qf, g, csg);          \
+    break;
+      HGQA_ROPE_CASE(1)
+      HGQA_ROPE_CASE(2)
+      HGQA_ROPE_CASE(3)
+      HGQA_ROPE_CASE(4)
+#undef HGQA_ROPE_CASE
+    }
+  } else {
+    // r/2 an odd multiple of 8: partner chunks are read again from HBM.
+    const float2* csrow = a.cs_table + (size_t)t_row * half;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int d0 = 16 * s + 8 * g;
+      float x[8];
+      unpack8(qraw[s], x);
+      if (d0 < rdims) {
+        const bool first = d0 < half;
+        const int i0 = first ? d0 : d0 - half;
+        u32x4_t praw = *reinterpret_cast<const u32x4_t*>(qrow + (first ? d0 + half : d0 - half));
+        rotate8(x, praw, csrow + i0, first ? -1.0f : 1.0f);
+      }
+      qf[s] = pack8(x);
+    }
+  }
+  if (cs_lds) __syncthreads();  // the cos/sin rows are read before K buffer 1 is refilled
+
   f32x16_t O[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) O[i] = f32x16_t{};
@@ -178,9 +257,6 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int vkey0 = 4 * g + (r16 >> 2);
   const int vd = 16 * dhalf + 4 * (r16 & 3);
 
-  if (ntiles > 0) load_tile(j_lo, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & 1;
@@ -226,16 +302,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * sc);
-    // Rescale the running output only when some row's maximum grew.
-    if (__any(m_new > m_run)) {
-      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // m_run is a per-row reference, not the exact running maximum: it moves
+    // only when a score exceeds it by more than 2^8, so probabilities stay
+    // below 256 and the output is rescaled rarely; O / l is exact for any
+    // reference.
+    const float m_cand = mx * sc;
+    const bool need = m_cand > m_run + 8.0f;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+      m_run = need ? m_cand : m_run;
     }
-    m_run = m_new;
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
     // P = exp2(S*sc - m), packed to bf16 in the B-operand order of PV; the
     // row sum is taken over the same rounded values.
@@ -369,9 +449,9 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const long long nrb = (TG + kRows - 1) / kRows;
   const long long blocks = nrb * a.B * a.Hkv;
   if (a.D == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 
