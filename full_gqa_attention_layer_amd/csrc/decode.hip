@@ -15,6 +15,8 @@
 // their (max, sum, output) in LDS; with one split the workgroup writes the
 // gated output, otherwise it writes a partial that the merge kernel combines
 // by log-sum-exp.
+#include <cstdlib>
+
 #include "device_util.h"
 
 namespace hgqa {
@@ -22,15 +24,41 @@ namespace hgqa {
 constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kChunk = 32;
-constexpr int kDecMinKeysPerBlock = kDecWaves * kChunk;
+constexpr int kDecMinKeysPerBlock = 1024;
 constexpr int kDecTargetBlocks = 2048;
 constexpr float kLog2eDec = 1.4426950408889634f;
 
+// Waits until at most N vector-memory loads of this wave are outstanding
+// (loads retire in order, so everything issued before the last N is done).
+template <int N>
+__device__ __forceinline__ void vm_wait_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else static_assert(N == 0 || N == 8 || N == 16, "add the count");
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// A V chunk sits in the wave's LDS buffer as [32 keys][D] bf16 rows with the
+// 16-byte chunk c of key row k at position c ^ vswz(k): the transposed reads
+// (ds_read_b64_tr_b16, 32 lanes = 8 key rows x 2 chunks) hit distinct banks.
+template <int D> struct DecSwz;
+template <> struct DecSwz<128> {
+  static __device__ __forceinline__ int v(int key) { return 2 * (key & 7); }
+};
+template <> struct DecSwz<64> {
+  static __device__ __forceinline__ int v(int key) { return 2 * ((key >> 1) & 3); }
+};
+
 template <int D>
 struct DecodeLds {
-  static constexpr int VSTR = kChunk + 8;  // bf16 per V^T row: 80 bytes
   union {
-    uint16_t vt[kDecWaves][D * VSTR];
+    uint16_t v[kDecWaves][2][kChunk * D];  // per-wave double-buffered V chunks
     struct {
       float o[kDecWaves][16][D];
       float m[kDecWaves][16];
@@ -45,13 +73,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   constexpr int NS = D / 32;          // k-steps of 32 dims
   constexpr int NDB = D / 16;         // 16-dim blocks of the output
   constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int KQ = 64 / CH;         // key quads covered by one pass of a wave
-  constexpr int QPL = 8 / KQ;         // key quads per lane (2 for D=128, 1 for D=64)
-  constexpr int VSTR = DecodeLds<D>::VSTR;
   __shared__ DecodeLds<D> sm;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, g = lane >> 4;
   const int Hkv = a.Hkv, G = a.G;
 
@@ -67,6 +93,45 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   const int k_begin = split * a.split_keys;
   if (k_begin >= n_vis) return;
   const int k_end = min(n_vis, k_begin + a.split_keys);
+
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
+
+  f32x4_t O[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) O[i] = f32x4_t{};
+  float m_run = -INFINITY, l_run = 0.0f;
+  const float sc = a.scale * kLog2eDec;
+
+  // Chunk loads: K straight into the MFMA A-operand layout (lane holds key
+  // n16 + 16 kb, dims 32s+8g..+7), V from HBM into the wave's LDS buffer.
+  // Keys past the split re-read its last key; their scores are masked.
+  constexpr int VDMA = kChunk * CH / 64;  // 1 KB HBM->LDS pieces per V chunk
+  auto issue = [&](int key0, u32x4_t (&kf)[2][NS], uint16_t* vbuf) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = min(key0 + 16 * kb + n16, k_end - 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        kf[kb][s] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + 32 * s + 8 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < VDMA; ++i) {
+      const int P = 64 * i + lane;
+      const int row = P / CH, pos = P % CH;
+      const int key = min(key0 + row, k_end - 1);
+      const uint16_t* src = vbase + (size_t)key * D + 8 * (pos ^ DecSwz<D>::v(row));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(vbuf + 512 * i), 16, 0, 0);
+    }
+  };
+
+  // The first chunk starts moving before q is rotated.
+  constexpr int STEP = kChunk * kDecWaves;
+  u32x4_t kfa[2][NS], kfb[2][NS];
+  uint16_t* va_buf = sm.u.v[wave][0];
+  uint16_t* vb_buf = sm.u.v[wave][1];
+  int key0 = k_begin + kChunk * wave;
+  if (key0 < k_end) issue(key0, kfa, va_buf);
 
   // ---- rotate q at position L-1; lane holds head n16, dims 32s+8g..+7
   const int half = a.rope.half, rdims = a.rope.rdims;
@@ -106,42 +171,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     }
   }
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
-  uint16_t* vt = sm.u.vt[wave];
-  const int kq = lane % KQ, dc = lane / KQ;
+  // V^T operand supplier addresses for ds_read_b64_tr_b16: lane r of each
+  // 16-lane group (group g) points at key 4g + r/4 and dims 4(r%4)..+3.
+  const int r16 = lane & 15;
+  const int vrow0 = 4 * g + (r16 >> 2);
+  const int vdim = 4 * (r16 & 3);
 
-  f32x4_t O[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) O[i] = f32x4_t{};
-  float m_run = -INFINITY, l_run = 0.0f;
-  const float sc = a.scale * kLog2eDec;
-
-  for (int key0 = k_begin + kChunk * wave; key0 < k_end; key0 += kChunk * kDecWaves) {
-    // K in A-operand layout: lane holds key n16 (+16 kb), dims 32s+8g..+7
-    u32x4_t kf[2][NS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = key0 + 16 * kb + n16;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        kf[kb][s] = (key < k_end)
-                        ? *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + 32 * s + 8 * g)
-                        : u32x4_t{0, 0, 0, 0};
-    }
-    // V rows: lane holds quads kq (+KQ), dims 8dc..8dc+7
-    u32x4_t vr[QPL][4];
-#pragma unroll
-    for (int qq = 0; qq < QPL; ++qq)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * (kq + KQ * qq) + i;
-        vr[qq][i] = (key < k_end)
-                        ? *reinterpret_cast<const u32x4_t*>(vbase + (size_t)key * D + 8 * dc)
-                        : u32x4_t{0, 0, 0, 0};
-      }
-
-    // scores
+  auto compute = [&](int key0, const u32x4_t (&kf)[2][NS], const uint16_t* vbuf) {
     f32x4_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -151,26 +187,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
         S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kb][s]),
                                                          qf[s], S[kb], 0, 0, 0);
     }
-
-    // V^T into this wave's LDS tile. Quad q of the chunk goes to column
-    // 8(q%4) + 4(q/4): the 8 keys a lane group feeds one product are adjacent.
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int qq = 0; qq < QPL; ++qq) {
-      const int q = kq + KQ * qq;
-      const int col = 8 * (q & 3) + 4 * (q >> 2);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t k0 = vr[qq][0][e], k1 = vr[qq][1][e], k2 = vr[qq][2][e], k3 = vr[qq][3][e];
-        u32x2_t lo = {(k0 & 0xffffu) | (k1 << 16), (k2 & 0xffffu) | (k3 << 16)};
-        u32x2_t hi = {(k0 >> 16) | (k1 & 0xffff0000u), (k2 >> 16) | (k3 & 0xffff0000u)};
-        const int d = 8 * dc + 2 * e;
-        *reinterpret_cast<u32x2_t*>(&vt[d * VSTR + col]) = lo;
-        *reinterpret_cast<u32x2_t*>(&vt[(d + 1) * VSTR + col]) = hi;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
     // mask keys past the split; online softmax per head (column n16)
     float mx = -INFINITY;
 #pragma unroll
@@ -201,12 +217,47 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     }
     l_run = fmaf(l_run, alpha, psum);
     const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk);
+    // O^T += V^T P^T: the A operand (16 dims x 32 keys) comes transposed out
+    // of LDS, keys 4g..4g+3 then 16+4g..16+4g+3 to match P's order.
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+      const int d = 16 * db + vdim;
+      const int c = d >> 3, hw = d & 7;
+      const int r0 = vrow0, r1 = vrow0 + 16;
+      const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(vbuf + r0 * D + 8 * (c ^ DecSwz<D>::v(r0)) + hw));
+      const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4_t*)(vbuf + r1 * D + 8 * (c ^ DecSwz<D>::v(r1)) + hw));
+      const i16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
       O[db] *= alpha;
-      bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(&vt[(16 * db + n16) * VSTR + 8 * g]);
-      O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, O[db], 0, 0, 0);
+      O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va), pb, O[db],
+                                                       0, 0, 0);
     }
+  };
+
+  // Double-buffered chunk loop: the next chunk's loads are in flight while
+  // the current one is computed. Unrolled by two so buffers are static.
+  while (key0 < k_end) {
+    const int k1 = key0 + STEP;
+    if (k1 < k_end) {
+      issue(k1, kfb, vb_buf);
+      vm_wait_keep<2 * NS + VDMA>();
+    } else {
+      vm_wait_keep<0>();
+    }
+    compute(key0, kfa, va_buf);
+    if (k1 >= k_end) break;
+    const int k2 = k1 + STEP;
+    __builtin_amdgcn_wave_barrier();  // buffer a is consumed before it is refilled
+    if (k2 < k_end) {
+      issue(k2, kfa, va_buf);
+      vm_wait_keep<2 * NS + VDMA>();
+    } else {
+      vm_wait_keep<0>();
+    }
+    compute(k1, kfb, vb_buf);
+    __builtin_amdgcn_wave_barrier();
+    key0 = k2;
   }
 
   // ---- merge the waves of this workgroup
@@ -356,8 +407,26 @@ DecodePlan plan_decode(Elem e, int B, int Hq, int Hkv, int D, int sliding, int w
     return p;
   }
   const long long pairs = (long long)B * Hkv;
+  // HGQA_DECODE_SPLIT_KEYS (tuning only) fixes the keys per split.
+  if (const char* env = getenv("HGQA_DECODE_SPLIT_KEYS")) {
+    long long sk = atoll(env);
+    if (sk > 0) {
+      sk = (sk + kChunk - 1) / kChunk * kChunk;
+      p.split_keys = (int)(sk < n_vis_max ? sk : (n_vis_max + kChunk - 1) / kChunk * kChunk);
+      p.num_splits = (n_vis_max + p.split_keys - 1) / p.split_keys;
+      p.workspace_bytes = p.num_splits > 1
+                              ? (size_t)B * Hq * p.num_splits * (size_t)(D + 2) * sizeof(float)
+                              : 0;
+      return p;
+    }
+  }
+  // Enough workgroups to fill the chip and balance unequal lengths, but no
+  // split below kDecMinKeysPerBlock keys when there are many (sequence, KV
+  // head) pairs: short splits cost a merge pass that a 512-slot ring does
+  // not repay.
   long long splits = (kDecTargetBlocks + pairs - 1) / pairs;
-  const long long max_splits = (n_vis_max + kDecMinKeysPerBlock - 1) / kDecMinKeysPerBlock;
+  const long long min_keys = pairs >= 256 ? kDecMinKeysPerBlock : kDecWaves * kChunk;
+  const long long max_splits = (n_vis_max + min_keys - 1) / min_keys;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   long long sk = (n_vis_max + splits - 1) / splits;
