@@ -195,6 +195,11 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     }
   }
 
+  // The gate logit is needed only at the end; fetch it now so its latency
+  // hides behind the tile loop.
+  const float gate_logit =
+      bf16_to_f32(static_cast<const uint16_t*>(a.gate)[(size_t)(b * T + t_row) * Hq + h]);
+
   // ---- Q^T fragments: lane holds row n, dims 16s+8g..+7, rotated below.
   const uint16_t* qrow = qp + ((size_t)(b * T + t_row) * Hq + h) * D;
   u32x4_t qraw[NS];
@@ -359,9 +364,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // ---- epilogue: normalise, gate, store bf16
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (row_ok) {
-    const uint16_t* gp = static_cast<const uint16_t*>(a.gate);
-    const float gv = bf16_to_f32(gp[(size_t)(b * T + t_row) * Hq + h]);
-    const float inv = sigmoidf_dev(gv) / l_tot;
+    const float inv = sigmoidf_dev(gate_logit) / l_tot;
     uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(b * T + t_row) * Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
