@@ -102,10 +102,19 @@ __device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t
   }
 }
 
+constexpr int kCsFloat2 = 1024;  // cos/sin rows of one row block: 8 KB
+
+// One stage holds a K tile and a V tile. Stage 1 first holds the block's Q
+// rows (kRows x D bf16 = kBN x 2D), stage 0 finally the output rows.
+template <int D>
+struct PrefillStage {
+  uint16_t k[kBN * D];
+  uint16_t v[kBN * D];
+};
 template <int D>
 struct PrefillLds {
-  uint16_t k[2][kBN * D];
-  uint16_t v[2][kBN * D];
+  PrefillStage<D> st[2];
+  float2 cs[kCsFloat2];
 };
 
 template <int D>
@@ -170,27 +179,49 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       const int j = min(j0 + key, T - 1);
       const uint16_t* ksrc = kbase + (size_t)j * D + 8 * (pos ^ Swz<D>::k(key));
       const uint16_t* vsrc = vbase + (size_t)j * vstride + 8 * (pos ^ Swz<D>::v(key));
-      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.k[st][512 * I], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.v[st][512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
     }
   };
 
   // The first K/V tile starts moving before anything else.
   if (ntiles > 0) load_tile(j_lo, 0);
 
-  // ---- cos/sin rows of the workgroup's positions go to LDS (the second K
-  // buffer is idle until the loop starts) when they fit; else Q reads them
-  // from the global table.
+  // Memory row R of the block (clamped to the last row): its Q / output row.
+  auto row_offset = [&](int R) -> size_t {
+    const int Rc = min(R, TG - 1);
+    const int t = Rc / G;
+    return ((size_t)(b * T + t) * Hq + kvh * G + (Rc - t * G)) * D;
+  };
+
+  // ---- the block's Q rows go to stage 1 (idle until the loop starts), four
+  // whole rows per 1 KB piece; chunk c of row r sits at position c ^ swz(r),
+  // the layout K tiles use, so the fragment reads below are conflict-free.
+  {
+    constexpr int Q_PIECES = kRows * D * 2 / 1024 / kWaves;
+    uint16_t* qs = reinterpret_cast<uint16_t*>(&sm.st[1]);
+#pragma unroll
+    for (int i = 0; i < Q_PIECES; ++i) {
+      const int I = wave * Q_PIECES + i;
+      const int Pc = 64 * I + lane;
+      const int r = Pc / CH, pos = Pc % CH;
+      const uint16_t* src = qp + row_offset(R0 + r) + 8 * (pos ^ Swz<D>::k(r));
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)&qs[512 * I], 16, 0, 0);
+    }
+  }
+
+  // ---- cos/sin rows of the workgroup's positions go to LDS when they fit;
+  // else Q reads them from the global table.
   const int half = a.rope.half, rdims = a.rope.rdims;
   const int cs_bytes = (t_hi - t_lo + 1) * half * 8;
-  const bool cs_lds = half > 0 && cs_bytes <= (int)sizeof(sm.k[1]);
+  const bool cs_lds = half > 0 && cs_bytes <= (int)sizeof(sm.cs);
   if (cs_lds) {
     const char* src0 = reinterpret_cast<const char*>(a.cs_table + (size_t)t_lo * half);
     const int nblk = (cs_bytes + 1023) / 1024;
     for (int I = wave; I < nblk; I += kWaves) {
       const int off = min(1024 * I + 16 * lane, cs_bytes - 16);
       __builtin_amdgcn_global_load_lds((const void*)(src0 + off),
-                                       (lds_void_t*)(reinterpret_cast<char*>(sm.k[1]) + 1024 * I),
+                                       (lds_void_t*)(reinterpret_cast<char*>(sm.cs) + 1024 * I),
                                        16, 0, 0);
     }
   }
@@ -200,13 +231,19 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   const float gate_logit =
       bf16_to_f32(static_cast<const uint16_t*>(a.gate)[(size_t)(b * T + t_row) * Hq + h]);
 
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // tile 0, the Q rows and the cos/sin rows have landed
+
   // ---- Q^T fragments: lane holds row n, dims 16s+8g..+7, rotated below.
   const uint16_t* qrow = qp + ((size_t)(b * T + t_row) * Hq + h) * D;
   u32x4_t qraw[NS];
+  {
+    const int r = wave * kRowsPerWave + n;
+    const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.st[1]) + r * D;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qraw[s] = *reinterpret_cast<const u32x4_t*>(qrow + 16 * s + 8 * g);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // tile 0 and the cos/sin rows have landed
+    for (int s = 0; s < NS; ++s)
+      qraw[s] = *reinterpret_cast<const u32x4_t*>(qs + 8 * ((2 * s + g) ^ Swz<D>::k(r)));
+  }
 
   bf16x8_t qf[NS];
   if (half == 0) {
@@ -215,7 +252,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   } else if (half % 16 == 0) {
     // The RoPE partner of every chunk sits in this lane, half/16 chunks away.
     const int tl = t_row - t_lo;
-    const float2* csl = reinterpret_cast<const float2*>(sm.k[1]) + tl * half;
+    const float2* csl = sm.cs + tl * half;
     const float2* csg = a.cs_table + (size_t)t_row * half;
     switch (half / 16) {
 #define HGQA_ROPE_CASE(H)                                 \
@@ -246,7 +283,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       qf[s] = pack8(x);
     }
   }
-  if (cs_lds) __syncthreads();  // the cos/sin rows are read before K buffer 1 is refilled
+  __syncthreads();  // Q and the cos/sin rows are read before stage 1 is refilled
 
   f32x16_t O[NDB];
 #pragma unroll
@@ -267,8 +304,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     const int st = it & 1;
     const int j0 = j_lo + it * kBN;
     if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
-    const uint16_t* ks = sm.k[st];
-    const uint16_t* vs = sm.v[st];
+    const uint16_t* ks = sm.st[st].k;
+    const uint16_t* vs = sm.st[st].v;
 
     // S^T for two 32-key blocks
     f32x16_t S[2];
@@ -361,20 +398,32 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     __syncthreads();
   }
 
-  // ---- epilogue: normalise, gate, store bf16
+  // ---- epilogue: normalise and gate in registers, then turn the O^T
+  // fragments into row-major rows in LDS (stage 0 is idle: the loop ended on
+  // a barrier with no load in flight) so that the stores write whole rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (row_ok) {
-    const float inv = sigmoidf_dev(gate_logit) / l_tot;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)(b * T + t_row) * Hq + h) * D;
+  const float inv = row_ok ? sigmoidf_dev(gate_logit) / l_tot : 0.0f;
+  uint16_t* ow = reinterpret_cast<uint16_t*>(&sm.st[0]) + wave * (kRowsPerWave * D);  // this wave's rows
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * g;
-        u32x2_t w = {pack_bf16x2(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv),
-                     pack_bf16x2(O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(orow + d) = w;
-      }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int c = 4 * db + q4;  // 16-byte chunk of dims 32 db + 8 q4 ..
+      u32x2_t w = {pack_bf16x2(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv),
+                   pack_bf16x2(O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv)};
+      *reinterpret_cast<u32x2_t*>(ow + n * D + 8 * (c ^ Swz<D>::k(n)) + 4 * g) = w;
+    }
+  __syncthreads();
+  constexpr int O_PIECES = kRowsPerWave * D * 2 / 1024;
+  uint16_t* op = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int i = 0; i < O_PIECES; ++i) {
+    const int Pc = 64 * i + lane;
+    const int r = Pc / CH, pos = Pc % CH;  // row of the wave, LDS position
+    const int R = R0 + wave * kRowsPerWave + r;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ow + r * D + 8 * pos);
+    if (R < TG)
+      *reinterpret_cast<u32x4_t*>(op + row_offset(R) + 8 * (pos ^ Swz<D>::k(r))) = v;
   }
 }
 
