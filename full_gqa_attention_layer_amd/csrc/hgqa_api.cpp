@@ -99,6 +99,52 @@ size_t prefill_ws(const Layer& l, int B, int T) {
   return round256((size_t)B * l.Hkv * T * l.D * l.esize) + round256((size_t)T * l.half * sizeof(float2));
 }
 
+// Checks shared by the prefill entry points; n = tokens in this call.
+int check_prefill_call(const Layer& l, int batch, int n, const void* q, const void* k,
+                       const void* v, const void* gate, const void* out, const void* workspace,
+                       size_t workspace_bytes) {
+  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
+  if ((long long)batch * n * l.Hq * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "problem too large");
+  const long long TG = (long long)n * l.G;
+  if (l.elem == hgqa::Elem::BF16 && (TG + 127) / 128 * batch * l.Hkv > 0x7fffffffLL)
+    return fail(HGQA_EUNSUPPORTED, "too many query blocks");
+  if (!q || !k || !v || !gate || !out || !workspace)
+    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return fail(HGQA_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
+  const size_t need = prefill_ws(l, batch, n);
+  if (workspace_bytes < need)
+    return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (out == q || out == k || out == v || out == gate)
+    return fail(HGQA_EINVAL, "out must not alias an input");
+  return HGQA_OK;
+}
+
+hgqa::PrefillArgs prefill_args(const Layer& l, int batch, int n, const void* q, const void* k,
+                               const void* v, const void* gate, void* out, void* workspace) {
+  hgqa::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.out = out;
+  a.k_rot = workspace;
+  a.cs_table = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                         round256((size_t)batch * l.Hkv * n * l.D * l.esize));
+  a.B = batch;
+  a.T = n;
+  a.Hq = l.Hq;
+  a.Hkv = l.Hkv;
+  a.G = l.G;
+  a.D = l.D;
+  a.sliding = l.sliding;
+  a.window = l.window;
+  a.scale = l.scale;
+  fill_rope(l, &a.rope);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,43 +165,79 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
   if (rc != HGQA_OK) return rc;
   if (batch < 0 || seq_len < 0) return fail(HGQA_EINVAL, "batch and seq_len must be >= 0");
   if (batch == 0 || seq_len == 0) return ok();
-  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
-  if ((long long)batch * seq_len * l.Hq * l.D > kMaxElems)
-    return fail(HGQA_EUNSUPPORTED, "problem too large");
-  const long long TG = (long long)seq_len * l.G;
-  if (l.elem == hgqa::Elem::BF16 && (TG + 127) / 128 * batch * l.Hkv > 0x7fffffffLL)
-    return fail(HGQA_EUNSUPPORTED, "too many query blocks");
-  if (!q || !k || !v || !gate || !out || !workspace)
-    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
-    return fail(HGQA_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
-  const size_t need = prefill_ws(l, batch, seq_len);
-  if (workspace_bytes < need)
-    return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
-  if (out == q || out == k || out == v || out == gate)
-    return fail(HGQA_EINVAL, "out must not alias an input");
-
-  hgqa::PrefillArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.gate = gate;
-  a.out = out;
-  a.k_rot = workspace;
-  a.cs_table = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                         round256((size_t)batch * l.Hkv * seq_len * l.D * l.esize));
-  a.B = batch;
-  a.T = seq_len;
-  a.Hq = l.Hq;
-  a.Hkv = l.Hkv;
-  a.G = l.G;
-  a.D = l.D;
-  a.sliding = l.sliding;
-  a.window = l.window;
-  a.scale = l.scale;
-  fill_rope(l, &a.rope);
+  rc = check_prefill_call(l, batch, seq_len, q, k, v, gate, out, workspace, workspace_bytes);
+  if (rc != HGQA_OK) return rc;
+  hgqa::PrefillArgs a = prefill_args(l, batch, seq_len, q, k, v, gate, out, workspace);
   hipError_t e = hgqa::launch_prefill(a, l.elem, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t n_new) {
+  return attn_prefill_workspace_bytes(layer, batch, n_new);
+}
+
+int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new, int32_t start_pos,
+                       const void* q, const void* k, const void* v, const void* gate,
+                       void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Layer l;
+  int rc = check_layer(layer, &l);
+  if (rc != HGQA_OK) return rc;
+  if (batch < 0 || n_new < 0 || start_pos < 0)
+    return fail(HGQA_EINVAL, "batch, n_new and start_pos must be >= 0");
+  if ((long long)start_pos + n_new > 0x7fffffffLL)
+    return fail(HGQA_EUNSUPPORTED, "start_pos + n_new exceeds int32");
+  if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
+  if (l.sliding && cache_capacity != l.window)
+    return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
+                l.window, cache_capacity);
+  if (!l.sliding && (long long)start_pos + n_new > cache_capacity)
+    return fail(HGQA_ENOSPACE, "positions up to %lld exceed the full cache capacity %d",
+                (long long)start_pos + n_new, cache_capacity);
+  if (batch == 0 || n_new == 0) return ok();
+  rc = check_prefill_call(l, batch, n_new, q, k, v, gate, out, workspace, workspace_bytes);
+  if (rc != HGQA_OK) return rc;
+  if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "cache too large");
+  if (!k_cache || !v_cache) return fail(HGQA_EINVAL, "a cache pointer is NULL");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(HGQA_EINVAL, "the caches must be 16-byte aligned");
+  const void* caches[2] = {k_cache, v_cache};
+  for (const void* c : caches)
+    if (c == q || c == k || c == v || c == gate || c == out || c == workspace)
+      return fail(HGQA_EINVAL, "a cache must not alias q, k, v, gate, out or the workspace");
+  if (k_cache == v_cache) return fail(HGQA_EINVAL, "k_cache and v_cache must differ");
+
+  // Attention first: a ring still holds the W - 1 positions before the chunk.
+  hgqa::PrefillArgs a = prefill_args(l, batch, n_new, q, k, v, gate, out, workspace);
+  a.p0 = start_pos;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cap = cache_capacity;
+  a.ring = l.sliding;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hgqa::launch_prefill(a, l.elem, s);
+  if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+
+  // Then the chunk joins the cache, as kv_append would leave it.
+  hgqa::AppendArgs ap{};
+  ap.start_pos = nullptr;
+  ap.start_uniform = start_pos;
+  ap.k_new = k;
+  ap.v_new = v;
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.B = batch;
+  ap.n_new = n_new;
+  ap.Hkv = l.Hkv;
+  ap.D = l.D;
+  ap.cap = cache_capacity;
+  ap.sliding = l.sliding;
+  ap.window = l.window;
+  ap.rope = a.rope;
+  e = hgqa::launch_kv_append(ap, l.elem, s);
+  if (e != hipSuccess) return fail(HGQA_EHIP, "kv_append launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -35,6 +35,13 @@ struct PrefillArgs {
   int sliding, window;
   float scale;          // softmax scale
   RopeArgs rope;
+  // Chunked prefill: row t of this call sits at absolute position p0 + t, and
+  // keys at positions < p0 come from the layer's cache ([B,Hkv,cap,D], K
+  // rotated; slot p, or p mod cap for a ring). Plain prefill: p0 = 0, no cache.
+  int p0;
+  const void* k_cache;
+  const void* v_cache;
+  int cap, ring;
 };
 
 // Rotated-K and cos/sin-table pre-pass, then the attention kernel.
@@ -42,7 +49,8 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s);
 
 // ---------------------------------------------------------------- kv append
 struct AppendArgs {
-  const int32_t* start_pos;  // [B]
+  const int32_t* start_pos;  // [B]; NULL: every sequence starts at start_uniform
+  int start_uniform;
   const void* k_new;         // [B,n,Hkv,D]
   const void* v_new;         // [B,n,Hkv,D]
   void* k_cache;             // [B,Hkv,cap,D]

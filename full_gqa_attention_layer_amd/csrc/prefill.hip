@@ -117,7 +117,8 @@ struct PrefillLds {
   float2 cs[kCsFloat2];
 };
 
-template <int D>
+// kCache: chunked prefill, keys before position p0 come from the cache.
+template <int D, bool kCache>
 __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int PER_WAVE = CH / kWaves;       // 1 KB loads per wave per operand per tile
@@ -153,32 +154,47 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   const int t_hi = (min(R0 + kRows, TG) - 1) / G;
   const int w0 = min(R0 + wave * kRowsPerWave, TG - 1);
   const int w1 = min(R0 + wave * kRowsPerWave + kRowsPerWave - 1, TG - 1);
-  const int tw_lo = w0 / G, tw_hi = w1 / G;
+  // Masks and key ranges use absolute positions: row t of this call sits at
+  // p0 + t, and so does key t of this call.
+  const int p0 = kCache ? a.p0 : 0;
+  const int tw_lo = p0 + w0 / G, tw_hi = p0 + w1 / G;
+  const int t_abs = p0 + t_row;
 
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kr = static_cast<const uint16_t*>(a.k_rot);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
 
-  // ---- key range of the workgroup
-  const int j_lo = a.sliding ? max(0, t_lo - a.window + 1) : 0;
-  const int ntiles = (t_hi + 1 - j_lo + kBN - 1) / kBN;
+  // ---- key range of the workgroup (absolute positions)
+  const int j_lo = a.sliding ? max(0, p0 + t_lo - a.window + 1) : 0;
+  const int ntiles = (p0 + t_hi + 1 - j_lo + kBN - 1) / kBN;
+  const int j_last = p0 + T - 1;
 
   const uint16_t* kbase = kr + (size_t)(b * Hkv + kvh) * T * D;
   const uint16_t* vbase = vp + ((size_t)b * T * Hkv + kvh) * D;
   const size_t vstride = (size_t)Hkv * D;
+  const size_t cache_head = kCache ? (size_t)(b * Hkv + kvh) * a.cap * D : 0;
 
   // HBM -> LDS without registers: each wave moves PER_WAVE 1 KB pieces of
   // both tiles. Keys past the end re-read the last key: finite values that
-  // the causal mask hides (their probabilities are exactly 0).
+  // the causal mask hides (their probabilities are exactly 0). In a chunk,
+  // keys before p0 come from the cache: slot j, or j mod cap in a ring.
   auto load_tile = [&](int j0, int st) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int I = wave * PER_WAVE + i;
       const int P = 64 * I + lane;
       const int key = P / CH, pos = P % CH;
-      const int j = min(j0 + key, T - 1);
-      const uint16_t* ksrc = kbase + (size_t)j * D + 8 * (pos ^ Swz<D>::k(key));
-      const uint16_t* vsrc = vbase + (size_t)j * vstride + 8 * (pos ^ Swz<D>::v(key));
+      const int j = min(j0 + key, j_last);
+      const uint16_t* ksrc;
+      const uint16_t* vsrc;
+      if (kCache && j < p0) {
+        const size_t off = cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
+        ksrc = static_cast<const uint16_t*>(a.k_cache) + off + 8 * (pos ^ Swz<D>::k(key));
+        vsrc = static_cast<const uint16_t*>(a.v_cache) + off + 8 * (pos ^ Swz<D>::v(key));
+      } else {
+        ksrc = kbase + (size_t)(j - p0) * D + 8 * (pos ^ Swz<D>::k(key));
+        vsrc = vbase + (size_t)(j - p0) * vstride + 8 * (pos ^ Swz<D>::v(key));
+      }
       __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
     }
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     if (need_mask) {
       // key j = j0 + 4g + off is visible iff 0 <= t_row - j < W (W = 2^31 when
       // full): one unsigned compare per element against a per-lane base.
-      const int base = t_row - j0 - 4 * g;
+      const int base = t_abs - j0 - 4 * g;
       const unsigned wlim = a.sliding ? (unsigned)a.window : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -367,9 +383,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       const int kb = ks4 >> 1, hh = ks4 & 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e], sc, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e + 1], sc, -m_use));
-        const bf16x2_t pv = {(__bf16)p0, (__bf16)p1};
+        const float pa = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e], sc, -m_use));
+        const float pb = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e + 1], sc, -m_use));
+        const bf16x2_t pv = {(__bf16)pa, (__bf16)pb};
         pk[ks4][e] = __builtin_bit_cast(uint32_t, pv);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pv, ones, l_run, false);
       }
@@ -450,32 +466,44 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
     qs[d] = x;
   }
   __syncthreads();
-  const int lo = a.sliding ? max(0, t - a.window + 1) : 0;
+  // Absolute positions: row t sits at p0 + t; keys before p0 (a chunk that
+  // continues a cached sequence) come from the cache, slot j or j mod cap.
+  const int p0 = a.p0, ta = p0 + t;
+  const int lo = a.sliding ? max(0, ta - a.window + 1) : 0;
   const float* kr = static_cast<const float*>(a.k_rot) + (size_t)(b * a.Hkv + kvh) * T * D;
   const float* v = static_cast<const float*>(a.v) + ((size_t)b * T * a.Hkv + kvh) * D;
   const size_t vstride = (size_t)a.Hkv * D;
+  const size_t cache_head = (size_t)(b * a.Hkv + kvh) * a.cap * D;
+  auto key_row = [&](int j) -> const float* {
+    if (j < p0) return static_cast<const float*>(a.k_cache) + cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
+    return kr + (size_t)(j - p0) * D;
+  };
+  auto value_row = [&](int j) -> const float* {
+    if (j < p0) return static_cast<const float*>(a.v_cache) + cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
+    return v + (size_t)(j - p0) * vstride;
+  };
   float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int j0 = lo; j0 <= t; j0 += 64) {
+  for (int j0 = lo; j0 <= ta; j0 += 64) {
     const int j = j0 + lane;
     float s = -INFINITY;
-    if (j <= t) {
-      const float* krow = kr + (size_t)j * D;
+    if (j <= ta) {
+      const float* krow = key_row(j);
       float dot = 0.0f;
       for (int d = 0; d < D; ++d) dot = fmaf(qs[d], krow[d], dot);
       s = dot * a.scale;
     }
     const float mn = fmaxf(m, wave_max(s));
     const float alpha = expf(m - mn);
-    const float p = (j <= t) ? expf(s - mn) : 0.0f;
+    const float p = (j <= ta) ? expf(s - mn) : 0.0f;
     l = l * alpha + wave_sum(p);
     ps[lane] = p;
     __syncthreads();
     o0 *= alpha;
     o1 *= alpha;
-    const int nk = min(64, t - j0 + 1);
+    const int nk = min(64, ta - j0 + 1);
     for (int jj = 0; jj < nk; ++jj) {
       const float pj = ps[jj];
-      const float* vrow = v + (size_t)(j0 + jj) * vstride;
+      const float* vrow = value_row(j0 + jj);
       o0 = fmaf(pj, vrow[lane], o0);
       if (lane + 64 < D) o1 = fmaf(pj, vrow[lane + 64], o1);
     }
@@ -500,10 +528,15 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const long long TG = (long long)a.T * a.G;
   const long long nrb = (TG + kRows - 1) / kRows;
   const long long blocks = nrb * a.B * a.Hkv;
-  if (a.D == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(kWaves * 64);
+  const bool cache = a.k_cache != nullptr;
+  if (a.D == 128) {
+    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

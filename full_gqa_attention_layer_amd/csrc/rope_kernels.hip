@@ -1,7 +1,8 @@
 // RoPE kernels that touch each key once:
 //  * the prefill pre-pass: rotates K into a head-major copy [B,Hkv,T,D] and
 //    writes the (cos, sin) table [T, r/2] that the attention kernel uses to
-//    rotate Q while loading it;
+//    rotate Q while loading it; row t sits at absolute position p0 + t (p0 > 0
+//    for a chunk that continues a cached sequence);
 //  * kv_append: rotates new keys at their absolute positions and scatters
 //    keys and values into the layer's cache, slot p (full layer) or p mod W
 //    (sliding layer ring).
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
   const int half = a.rope.half;
   for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
     int tp = e / half, i = e - tp * half;
-    float2 c = rope_cos_sin(t0 + tp, a.rope.freq_over_pi[i]);
+    float2 c = rope_cos_sin(a.p0 + t0 + tp, a.rope.freq_over_pi[i]);
     cs[tp][i] = c;
     if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
   }
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
   const int half = a.rope.half, rdims = a.rope.rdims;
   for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
     int tp = e / half, i = e - tp * half;
-    float2 c = rope_cos_sin(t0 + tp, a.rope.freq_over_pi[i]);
+    float2 c = rope_cos_sin(a.p0 + t0 + tp, a.rope.freq_over_pi[i]);
     cs[tp][i] = c;
     if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
   }
@@ -134,7 +135,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __shared__ float2 cs[kMaxHalfRotary];
   const int n = blockIdx.x, b = blockIdx.y;
-  const int start = a.start_pos[b];
+  const int start = a.start_pos ? a.start_pos[b] : a.start_uniform;
   const int p = start + n;
   if (p < 0) return;
   int slot;

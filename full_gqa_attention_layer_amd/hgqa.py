@@ -20,8 +20,9 @@ FULL, SLIDING = 0, 1
 BF16, FP32 = 0, 1
 OK, EINVAL, EUNSUPPORTED, ENOSPACE, EHIP = 0, -1, -2, -3, -4
 
-EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "kv_append",
-            "attn_decode_workspace_bytes", "attn_decode", "hgqa_last_error")
+EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "attn_prefill_chunk_workspace_bytes",
+            "attn_prefill_chunk", "kv_append", "attn_decode_workspace_bytes", "attn_decode",
+            "hgqa_last_error")
 
 
 class HgqaLayer(ctypes.Structure):
@@ -57,6 +58,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_prefill_workspace_bytes.restype = S
     lib.attn_prefill.argtypes = [LP, I, I, P, P, P, P, P, P, S, P]
     lib.attn_prefill.restype = ctypes.c_int
+    lib.attn_prefill_chunk_workspace_bytes.argtypes = [LP, I, I]
+    lib.attn_prefill_chunk_workspace_bytes.restype = S
+    lib.attn_prefill_chunk.argtypes = [LP, I, I, I, P, P, P, P, P, P, I, P, P, S, P]
+    lib.attn_prefill_chunk.restype = ctypes.c_int
     lib.kv_append.argtypes = [LP, I, I, P, I, P, P, P, P, I, P]
     lib.kv_append.restype = ctypes.c_int
     lib.attn_decode_workspace_bytes.argtypes = [LP, I, I, I]
@@ -139,6 +144,36 @@ def attn_prefill(L: HgqaLayer, q, k, v, gate, out=None, workspace=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.attn_prefill(ctypes.byref(L), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                             _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def attn_prefill_chunk_workspace_bytes(L: HgqaLayer, batch: int, n_new: int) -> int:
+    return int(load_library().attn_prefill_chunk_workspace_bytes(ctypes.byref(L), batch, n_new))
+
+
+def attn_prefill_chunk(L: HgqaLayer, start_pos: int, q, k, v, gate, k_cache, v_cache,
+                       out=None, workspace=None):
+    """New tokens at start_pos.. over the cache and themselves, then appended (see hgqa.h)."""
+    lib = load_library()
+    B, n, Hq, D = q.shape
+    Hkv = Hq // max(L.gqa_ratio, 1)
+    cap = k_cache.shape[2]
+    dt = _torch_dtype(L)
+    _need(q, "q", (B, n, L.num_q_heads, L.head_dim), dt)
+    _need(k, "k", (B, n, Hkv, D), dt)
+    _need(v, "v", (B, n, Hkv, D), dt)
+    _need(gate, "gate", (B, n, Hq), dt)
+    _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
+    _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", (B, n, Hq, D), dt)
+    need = attn_prefill_chunk_workspace_bytes(L, B, n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_prefill_chunk(ctypes.byref(L), B, n, int(start_pos), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(gate), _ptr(k_cache), _ptr(v_cache), cap, _ptr(out),
+                                  _ptr(workspace), workspace.numel(), _stream()))
     return out
 
 

@@ -121,6 +121,46 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len,
                  void* stream);
 
 /*
+ * Scratch bytes attn_prefill_chunk needs: the same as attn_prefill for a
+ * prompt of n_new tokens.
+ */
+size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch,
+                                          int32_t n_new);
+
+/*
+ * Chunked prefill: n_new new tokens per sequence, at absolute positions
+ * start_pos .. start_pos + n_new - 1, attend over the layer's cache (the
+ * positions before start_pos) and over themselves; then they are appended to
+ * the cache. The result is what attn_prefill over the whole sequence gives for
+ * these rows. The cache-backed prefill the model pages leave to the full
+ * implementation ("Step-3.7-Flash-oQ3e" walkthrough, section 6) and the
+ * sliding cache of section 2.2 of the same page.
+ *   start_pos [host]      same for every sequence, >= 0
+ *   q     [B, n, Hq, D]   queries, not rotated
+ *   k, v  [B, n, Hkv, D]  new keys (not rotated) and values
+ *   gate  [B, n, Hq]      gate logits
+ *   k_cache, v_cache [B, Hkv, cap, D]  as kv_append fills them: rotated keys
+ *         and values of positions < start_pos. Full layer: slot p holds
+ *         position p, and cap >= start_pos + n. Sliding layer: cap == W and
+ *         slot p mod W holds position p for the last W positions before
+ *         start_pos (every earlier position the new rows can see).
+ *   out   [B, n, Hq, D]   gated attention output
+ *   workspace            >= attn_prefill_chunk_workspace_bytes(layer, B, n)
+ * In stream order the attention reads the cache before the append writes it,
+ * so a ring may be overwritten by its own chunk. The caches must not alias any
+ * other argument. n_new == 0 or batch == 0 does nothing. A multi-token decode
+ * step (one token plus draft tokens, each seeing the cache and the earlier new
+ * tokens) is this call with a small n_new. Errors: as attn_prefill, plus
+ * HGQA_ENOSPACE when a full cache is too small and HGQA_EINVAL when a ring's
+ * capacity differs from W.
+ */
+int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
+                       int32_t start_pos, const void* q, const void* k, const void* v,
+                       const void* gate, void* k_cache, void* v_cache,
+                       int32_t cache_capacity, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
  * Append new tokens to a layer's KV cache.
  *   start_pos    [B] int32  absolute position of k_new[b, 0]; >= 0
  *   max_end_pos  [host]     >= start_pos[b] + n_new for every b

@@ -96,6 +96,28 @@ def test_prefill_workspace_formula(lib):
     assert lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 1, 256) == 256 * 64 * 4 + 256 * 32 * 8
 
 
+def test_prefill_chunk_argument_checks(lib):
+    p, o, c1, c2 = (ctypes.c_void_p(x) for x in (256, 4096, 8192, 12288))
+    ws = 1 << 30
+
+    def call(L, B=1, n=4, p0=10, cap=512, kc=c1, vc=c2, wsb=ws):
+        return lib.attn_prefill_chunk(ctypes.byref(L), B, n, p0, p, p, p, p, kc, vc, cap, o, p,
+                                      wsb, None)
+    Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    assert call(Ls, cap=256) == hgqa.EINVAL          # a ring holds exactly W slots
+    assert call(Lf, cap=13) == hgqa.ENOSPACE          # 10 + 4 positions need 14 slots
+    assert call(Lf, p0=-1) == hgqa.EINVAL
+    assert call(Lf, n=0) == hgqa.OK                   # nothing to do
+    assert call(Lf, B=0) == hgqa.OK
+    assert call(Lf, kc=c1, vc=c1) == hgqa.EINVAL      # the caches must differ
+    assert call(Lf, kc=o) == hgqa.EINVAL              # a cache must not alias out
+    assert call(Lf, kc=ctypes.c_void_p(0)) == hgqa.EINVAL
+    assert call(Lf, wsb=1) == hgqa.ENOSPACE
+    assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), 2, 100) == \
+        lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 2, 100)
+
+
 def test_kv_append_argument_checks(lib):
     p = ctypes.c_void_p(256)
     Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)

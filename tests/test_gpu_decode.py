@@ -110,6 +110,11 @@ SMALL = [
     (LayerShape(FULL, 0, 8, 2, 64, 1e4, 0.25), hgqa.BF16, [1, 129, 4000]),
     (LayerShape(SLIDING, 64, 4, 1, 64, 1e4, 1.0), hgqa.FP32, [10, 64, 100]),
     (LayerShape(FULL, 0, 6, 2, 128, 5e6, 0.5), hgqa.FP32, [1, 77, 300]),
+    # the pages' other layers: Step's 96-head sliding layers (G = 12, W = 512) and
+    # Muse's sliding (G = 16, W = 2048, base 5e5) and full (base 0) layers
+    (LayerShape(SLIDING, 512, 96, 8, 128, 1e4, 1.0), hgqa.BF16, [100, 512, 2000]),
+    (LayerShape(SLIDING, 2048, 32, 2, 128, 5e5, 1.0), hgqa.BF16, [700, 2048, 5000]),
+    (LayerShape(FULL, 0, 32, 2, 128, 0.0, 1.0), hgqa.BF16, [3000, 9000]),
 ]
 
 
