@@ -9,12 +9,15 @@ One step is one pass of the whole path over the Step-3.7-Flash sliding layer
 pair) per second of step time. Decode bandwidth is measured beside it on
 the batched-decode workload (64 sequences, contexts U[65536, 131072], full
 layer over a contiguous cache and sliding layer over 512-slot rings) and
-reported under "decode". The CPU oracle is timed on a bounded sample of the
-same prefill (whole KV groups of the layer) and reported under
-"cpu_baseline".
+reported under "decode", together with a multi-token step (one token plus
+three drafts per sequence, through attn_prefill_chunk) on the full layer's
+caches. Chunked prefill (2048 new tokens over a 30720-token cache on the Step
+full layer) is reported under "chunked_prefill". The CPU oracle is timed on a
+bounded sample of the same prefill (whole KV groups of the layer) and
+reported under "cpu_baseline".
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
-                    [--no-cpu-baseline] [--only prefill|decode|copy]
+                    [--no-cpu-baseline] [--only prefill|decode|chunk|copy]
 """
 from __future__ import annotations
 
@@ -39,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    p.add_argument("--only", choices=["prefill", "decode", "chunk", "copy"], default=None,
                    help="copy: a plain 1 GiB device copy, the reference kernel for "
                         "scaling HBM byte counters")
     p.add_argument("--cpu-groups", type=int, default=8,
@@ -221,9 +224,79 @@ def bench_decode(args, torch, hgqa, synth, workloads, acc):
                         + (f"{shape.window}-slot ring x {nsets} sets" if sliding
                            else f"contiguous cache, lengths U[{wl.min_seq_len},{wl.seq_len}]"),
         }
+        if not sliding:
+            res["multi_token_full"] = bench_multi_token(args, torch, hgqa, synth, acc, L, caches[0],
+                                                        key)
         del caches
         torch.cuda.empty_cache()
     return res
+
+
+def bench_multi_token(args, torch, hgqa, synth, acc, L, cache, key):
+    """A multi-token decode step (one token plus three drafts, causal among
+    themselves) through attn_prefill_chunk, on the full layer's caches: every
+    sequence at position 98300, the mean context of the batched workload."""
+    kc, vc = cache
+    B, Hkv, cap, D = kc.shape
+    Hq, n, p0 = L.num_q_heads, 4, 98300
+    dev = kc.device
+    q = synth.host_normal((B, n, Hq, D), key + (synth.Q, 1)).to(dev)
+    g = synth.host_normal((B, n, Hq), key + (synth.GATE, 1)).to(dev)
+    kn = synth.host_normal((B, n, Hkv, D), key + (synth.NEW_K, 1)).to(dev)
+    vn = synth.host_normal((B, n, Hkv, D), key + (synth.NEW_V, 1)).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, B, n), dtype=torch.uint8, device=dev)
+    timer = EventTimer(torch)
+    for i in range(args.warmup + args.steps):
+        if i >= args.warmup:
+            with timer:
+                hgqa.attn_prefill_chunk(L, p0, q, kn, vn, g, kc, vc, out=out, workspace=ws)
+        else:
+            hgqa.attn_prefill_chunk(L, p0, q, kn, vn, g, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    nbytes = B * (p0 + n) * Hkv * D * 2 * 2 + 2 * q.numel() * 2 + g.numel() * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": ms, "GB/s": gbps, "frac_hbm": gbps / acc.PEAK_HBM_GBPS,
+            "workload": f"{B} sequences at position {p0}, {n} new tokens each (1 + 3 drafts), "
+                        f"{Hq} Q / {Hkv} KV heads, D{D}, full layer; attn_prefill_chunk incl. "
+                        "the append of the 4 tokens"}
+
+
+def bench_chunk(args, torch, hgqa, synth, workloads, acc):
+    """Chunked prefill: the last 2048 tokens of the Step full layer's
+    T = 32768 prompt, after the first 30720 are in the cache."""
+    shape = workloads.STEP_FULL.layers[0]
+    Hq, Hkv, D = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    p0, n = 30720, 2048
+    dev = torch.device("cuda:0")
+    key = (0, workloads.STEP_FULL.wid, 0, 9)
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    kc = torch.empty(1, Hkv, p0 + n, D, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    synth.device_normal_(kc, key + (synth.CACHE_K,))
+    synth.device_normal_(vc, key + (synth.CACHE_V,))
+    q = synth.host_normal((1, n, Hq, D), key + (synth.Q,)).to(dev)
+    k = synth.host_normal((1, n, Hkv, D), key + (synth.K,)).to(dev)
+    v = synth.host_normal((1, n, Hkv, D), key + (synth.V,)).to(dev)
+    g = synth.host_normal((1, n, Hq), key + (synth.GATE,)).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, 1, n), dtype=torch.uint8, device=dev)
+    timer = EventTimer(torch)
+    for i in range(args.warmup + min(args.steps, 10)):
+        if i >= args.warmup:
+            with timer:
+                hgqa.attn_prefill_chunk(L, p0, q, k, v, g, kc, vc, out=out, workspace=ws)
+        else:
+            hgqa.attn_prefill_chunk(L, p0, q, k, v, g, kc, vc, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    pairs = n * p0 + n * (n + 1) // 2
+    tflops = 4 * D * Hq * pairs / (ms * 1e-3) / 1e12
+    return {"ms": ms, "TFLOP/s": tflops, "frac_mfma": tflops / acc.PEAK_BF16_TFLOPS,
+            "workload": f"Step full layer (64 Q / 8 KV, D128, base 5e6, rotary 0.5): {n} new "
+                        f"tokens at positions {p0}..{p0 + n - 1} over a {p0}-token cache; "
+                        "attn_prefill_chunk incl. the append"}
 
 
 def cpu_baseline(args, torch, synth, workloads, acc):
@@ -285,16 +358,20 @@ def main():
     rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) inputs at the layer shapes; no weights)"}
-    if args.only != "decode":
+    if args.only in (None, "prefill"):
         r = bench_step(args, torch, hgqa, synth, workloads, acc)
         rec.update({"value": r["value"], "unit": "TFLOP/s", "ms_per_step": r["ms_per_step"],
                     "config": r["config"], "roofline": r["roofline"],
                     "prefill_ms": r["prefill_ms"]})
         print(f"[bench] step {r['ms_per_step']:.4f} ms, prefill {r['prefill_ms']:.4f} ms, "
               f"{r['roofline']['achieved']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-    if not args.no_decode and args.only != "prefill":
+    if not args.no_decode and args.only in (None, "decode"):
         rec["decode"] = bench_decode(args, torch, hgqa, synth, workloads, acc)
         print(f"[bench] decode {json.dumps(rec['decode'])}", file=sys.stderr, flush=True)
+    if args.only is None or args.only == "chunk":
+        rec["chunked_prefill"] = bench_chunk(args, torch, hgqa, synth, workloads, acc)
+        print(f"[bench] chunked prefill {json.dumps(rec['chunked_prefill'])}", file=sys.stderr,
+              flush=True)
     if not args.no_cpu_baseline and args.only is None:
         rec["cpu_baseline"] = cpu_baseline(args, torch, synth, workloads, acc)
     print(json.dumps(rec), flush=True)
