@@ -10,6 +10,7 @@ from .attention import (  # noqa: F401
     cached_positions,
     decode,
     kv_append,
+    llama3_frequencies,
     prefill,
     prefill_rows,
     rope,

@@ -19,6 +19,9 @@ Sources (pages as published; sections as headed on each page):
        fields": num_attention_heads 64, num_attention_groups 8, head_dim 128,
        sliding_window 512, rope_theta per layer, partial_rotary_factors,
        use_head_wise_attn_gate, sink false.
+  [P1] 2.3 also: long-context frequency scaling ("rope_type llama3", factor
+       2.0) is mounted on full layers only; sliding layers keep the default
+       RoPE.
   [P4] "Muse-Glimmer-30B-6bit" architecture walkthrough (discosf.com),
        sections "each layer: double LayerNorm + gated attention" (gate_proj is
        a sigmoid gate on the attention output), "GQA 16:1", "sliding window
@@ -36,7 +39,11 @@ Readings taken where the pages are silent (each is a choice, not a page fact):
   * Q head h reads KV head floor(h / G) ([P2] 64 heads in 8 groups);
   * one gate logit per (token, head); out = sigmoid(gate) * attention
     ([P1] 2.3, [P4] gated attention);
-  * softmax scale defaults to 1/sqrt(D); plain softmax with no sink ([P2]).
+  * softmax scale defaults to 1/sqrt(D); plain softmax with no sink ([P2]);
+  * the "llama3" frequency scaling of [P1] 2.3 is the published Llama 3.1
+    rule (see llama3_frequencies); the pages give only its factor, so the
+    other three parameters are readings: low_freq_factor 1, high_freq_factor
+    4 and an original context of 131072 positions (262144 / factor).
 """
 from __future__ import annotations
 
@@ -64,6 +71,9 @@ class LayerSpec:
     rope_theta      base; 0 means no rotation ([P4] "the RoPE zero value")
     rotary_fraction f; r = round(f*D) leading dims rotate ([P1] 2.3)
     softmax_scale   None means 1/sqrt(D)
+    rope_scaling    None, or (factor, low_freq_factor, high_freq_factor,
+                    original_max_positions) of the "llama3" frequency scaling;
+                    applied on full layers only ([P1] 2.3)
     """
 
     layer_type: str
@@ -74,6 +84,7 @@ class LayerSpec:
     rope_theta: float
     rotary_fraction: float = 1.0
     softmax_scale: float | None = None
+    rope_scaling: tuple | None = None
 
     @property
     def gqa_ratio(self) -> int:
@@ -89,6 +100,13 @@ class LayerSpec:
             return 1.0 / math.sqrt(self.head_dim)
         return float(self.softmax_scale)
 
+    @property
+    def frequency_scaling(self):
+        """The scaling this layer's RoPE uses: none on sliding layers ([P1] 2.3)."""
+        if self.layer_type != FULL or self.rope_scaling is None:
+            return None
+        return self.rope_scaling
+
 
 def sigmoid(x):
     """Logistic function 1/(1+e^-x): the per-head gate of [P1] 2.3 and [P4]."""
@@ -96,13 +114,36 @@ def sigmoid(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
-def rope(x, positions, theta: float, rotary_dims: int):
+def llama3_frequencies(omega, factor: float, low_freq_factor: float,
+                       high_freq_factor: float, original_max_positions: float):
+    """The "llama3" rescaling of RoPE frequencies ([P1] 2.3 names it, with
+    factor 2.0, as the full layers' long-context extension).
+
+    Per frequency w, with wavelength 2*pi/w and an original context length
+    N: a wavelength shorter than N / high_freq_factor keeps w; one longer
+    than N / low_freq_factor gets w / factor; in between, w is blended
+    linearly, s = (N / wavelength - low_freq_factor) /
+    (high_freq_factor - low_freq_factor), giving (1 - s) * w / factor + s * w.
+    """
+    w = np.asarray(omega, dtype=np.float64)
+    if factor <= 1.0:
+        return w.copy()
+    wavelength = 2.0 * math.pi / w
+    s = (original_max_positions / wavelength - low_freq_factor) / (high_freq_factor - low_freq_factor)
+    blended = (1.0 - s) * w / factor + s * w
+    out = np.where(wavelength > original_max_positions / low_freq_factor, w / factor, blended)
+    return np.where(wavelength < original_max_positions / high_freq_factor, w, out)
+
+
+def rope(x, positions, theta: float, rotary_dims: int, scaling=None):
     """Rotary position embedding of x at the given absolute positions.
 
     x has shape [..., D]; positions broadcasts against x[..., 0]. For
-    i < r/2 the pair (x_i, x_{i+r/2}) is rotated by the angle p * theta^(-2i/r);
+    i < r/2 the pair (x_i, x_{i+r/2}) is rotated by the angle p * w_i with
+    w_i = theta^(-2i/r), rescaled by llama3_frequencies when scaling is given;
     dims r..D-1 are copied. theta == 0 or r == 0 returns x unchanged
-    ([P1] 2.3 per-layer base and partial rotary; [P4] "the RoPE zero value").
+    ([P1] 2.3 per-layer base, partial rotary and the full layers' scaling;
+    [P4] "the RoPE zero value").
     """
     x = np.asarray(x, dtype=np.float64)
     out = x.copy()
@@ -113,6 +154,8 @@ def rope(x, positions, theta: float, rotary_dims: int):
     half = rotary_dims // 2
     i = np.arange(half, dtype=np.float64)
     omega = np.power(float(theta), -2.0 * i / rotary_dims)
+    if scaling is not None:
+        omega = llama3_frequencies(omega, *scaling)
     angle = np.asarray(positions, dtype=np.float64)[..., None] * omega
     c = np.cos(angle)
     s = np.sin(angle)
@@ -168,8 +211,8 @@ def prefill(q, k, v, gate, layer: LayerSpec, return_probs: bool = False):
     B, T, Hq, D = q.shape
     G = layer.gqa_ratio
     pos = np.arange(T, dtype=np.float64)
-    qr = rope(q, pos[None, :, None], layer.rope_theta, layer.rotary_dims)
-    kr = rope(k, pos[None, :, None], layer.rope_theta, layer.rotary_dims)
+    qr = rope(q, pos[None, :, None], layer.rope_theta, layer.rotary_dims, layer.frequency_scaling)
+    kr = rope(k, pos[None, :, None], layer.rope_theta, layer.rotary_dims, layer.frequency_scaling)
     y = np.zeros((B, T, Hq, D), dtype=np.float64)
     probs = np.zeros((B, Hq, T, T), dtype=np.float64) if return_probs else None
     for b in range(B):
@@ -214,9 +257,9 @@ def prefill_rows(q, k, v, gate, layer: LayerSpec, rows):
         if key not in rotated:
             kk = np.asarray(k[b, :, kv], dtype=np.float64)
             rotated[key] = rope(kk, np.arange(T, dtype=np.float64),
-                                layer.rope_theta, r)
+                                layer.rope_theta, r, layer.frequency_scaling)
         qi = rope(np.asarray(q[b, t, h], dtype=np.float64), float(t),
-                  layer.rope_theta, r)
+                  layer.rope_theta, r, layer.frequency_scaling)
         s = layer.scale * (rotated[key][lo:t + 1] @ qi)
         a, _ = _softmax_attend(s[None, :], np.asarray(v[b, lo:t + 1, kv], dtype=np.float64))
         out[n] = sigmoid(float(gate[b, t, h])) * a[0]
@@ -251,7 +294,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, start_pos, layer: LayerSpec):
                     raise ValueError("position beyond the full cache")
                 slot = p
             kc[b, :, slot] = rope(np.asarray(k_new[b, n], dtype=np.float64), float(p),
-                                  layer.rope_theta, layer.rotary_dims)
+                                  layer.rope_theta, layer.rotary_dims, layer.frequency_scaling)
             vc[b, :, slot] = np.asarray(v_new[b, n], dtype=np.float64)
     return kc, vc
 
@@ -283,7 +326,7 @@ def decode(q, gate, k_cache, v_cache, seq_lens, layer: LayerSpec):
     for b in range(B):
         L = int(seq_lens[b])
         _, slots = cached_positions(L, layer, cap)
-        qr = rope(q[b], float(L - 1), layer.rope_theta, layer.rotary_dims)
+        qr = rope(q[b], float(L - 1), layer.rope_theta, layer.rotary_dims, layer.frequency_scaling)
         for h in range(Hq):
             kv = h // G
             kk = np.asarray(k_cache[b, kv, slots], dtype=np.float64)

@@ -335,3 +335,59 @@ def test_round_bf16_matches_library_and_ties():
     assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0                  # tie to even
     assert oracle.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # tie to even (up)
     assert oracle.round_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -40)) == -(1.0 + 2.0 ** -7)
+
+
+# ---- "llama3" frequency scaling of the full layers ([P1] 2.3; parameters
+# other than the factor are readings, see the oracle's header)
+
+def test_llama3_frequencies_regimes_by_hand():
+    N, f = 1000.0, 2.0
+    w = lambda wavelength: 2.0 * np.pi / wavelength
+    got = oracle.llama3_frequencies(np.array([w(200.0), w(2000.0), w(400.0)]), f, 1.0, 4.0, N)
+    # wavelength N/5 < N/4 keeps w; 2N > N halves it; N/2.5 blends with s = 0.5
+    np.testing.assert_allclose(got, [w(200.0), w(2000.0) / 2.0, 0.75 * w(400.0)], rtol=1e-15)
+
+
+def test_llama3_frequencies_identity_and_continuity():
+    w = 2.0 * np.pi / np.geomspace(10.0, 1e6, 200)
+    np.testing.assert_array_equal(oracle.llama3_frequencies(w, 1.0, 1.0, 4.0, 8192.0), w)
+    N = 8192.0
+    for edge, expect in ((N / 4.0, 1.0), (N, 0.5)):     # blend meets both plain regimes
+        we = 2.0 * np.pi / edge
+        for eps in (1 - 1e-9, 1 + 1e-9):
+            got = oracle.llama3_frequencies(np.array([we * eps]), 2.0, 1.0, 4.0, N)[0]
+            assert abs(got / (we * eps) - expect) < 1e-6
+
+
+def test_llama3_frequencies_stay_ordered():
+    i = np.arange(32.0)
+    w = 5e6 ** (-2.0 * i / 64.0)
+    s = oracle.llama3_frequencies(w, 2.0, 1.0, 4.0, 131072.0)
+    assert np.all(np.diff(s) < 0)
+    assert np.all(s <= w) and np.all(s >= w / 2.0)
+
+
+def test_scaled_rope_scores_depend_only_on_offset():
+    rng = np.random.default_rng(7)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    sc = (2.0, 1.0, 4.0, 64.0)
+    base = oracle.rope(q, 37.0, 1e4, 64, sc) @ oracle.rope(k, 11.0, 1e4, 64, sc)
+    for shift in (1.0, 250.0, 1e5):
+        s = oracle.rope(q, 37.0 + shift, 1e4, 64, sc) @ oracle.rope(k, 11.0 + shift, 1e4, 64, sc)
+        assert abs(s - base) < 1e-9 * max(1.0, abs(base))
+    plain = oracle.rope(q, 37.0, 1e4, 64) @ oracle.rope(k, 11.0, 1e4, 64)
+    assert abs(plain - base) > 1e-3          # the scaling does change scores
+
+
+def test_scaling_applies_to_full_layers_only():
+    rng = np.random.default_rng(8)
+    B, T, Hq, Hkv, D = 1, 40, 2, 1, 16
+    q, k, v = (rng.standard_normal((B, T, h, D)) for h in (Hq, Hkv, Hkv))
+    g = rng.standard_normal((B, T, Hq))
+    sc = (2.0, 1.0, 4.0, 16.0)
+    s_plain = oracle.prefill(q, k, v, g, LayerSpec(SLIDING, 8, Hq, Hkv, D, 1e4, 1.0))
+    s_sc = oracle.prefill(q, k, v, g, LayerSpec(SLIDING, 8, Hq, Hkv, D, 1e4, 1.0, None, sc))
+    np.testing.assert_array_equal(s_plain, s_sc)
+    f_plain = oracle.prefill(q, k, v, g, LayerSpec(FULL, 0, Hq, Hkv, D, 1e4, 1.0))
+    f_sc = oracle.prefill(q, k, v, g, LayerSpec(FULL, 0, Hq, Hkv, D, 1e4, 1.0, None, sc))
+    assert np.abs(f_plain - f_sc).max() > 1e-3
