@@ -37,6 +37,8 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 struct Layer {
   int sliding, window, Hq, G, Hkv, D, rdims, half;
   float theta, scale;
+  // llama3 frequency scaling (full layers); factor <= 1: none
+  double scale_factor, low_freq, high_freq, original_positions;
   hgqa::Elem elem;
   size_t esize;
 };
@@ -80,15 +82,39 @@ int check_layer(const hgqa_layer* L, Layer* out) {
   o.rdims = r;
   o.half = r / 2;
   o.scale = L->softmax_scale > 0.0f ? L->softmax_scale : (float)(1.0 / std::sqrt((double)o.D));
+  if (!std::isfinite(L->rope_scaling_factor) || !std::isfinite(L->rope_low_freq_factor) ||
+      !std::isfinite(L->rope_high_freq_factor))
+    return fail(HGQA_EINVAL, "rope scaling parameters must be finite");
+  // Only full layers carry the scaling; sliding layers keep the plain RoPE.
+  o.scale_factor = (!o.sliding && L->rope_scaling_factor > 1.0f) ? L->rope_scaling_factor : 1.0;
+  o.low_freq = L->rope_low_freq_factor > 0.0f ? L->rope_low_freq_factor : 1.0;
+  o.high_freq = L->rope_high_freq_factor > 0.0f ? L->rope_high_freq_factor : 4.0;
+  o.original_positions = L->rope_original_max_positions > 0 ? L->rope_original_max_positions : 131072.0;
+  if (o.scale_factor > 1.0 && !(o.high_freq > o.low_freq))
+    return fail(HGQA_EINVAL, "rope_high_freq_factor (%g) must exceed rope_low_freq_factor (%g)",
+                o.high_freq, o.low_freq);
   return HGQA_OK;
+}
+
+// Frequency w of a RoPE pair after the llama3 long-context rescaling: short
+// wavelengths keep w, long ones get w / factor, a linear blend in between.
+double llama3_frequency(const Layer& l, double w) {
+  const double wavelength = 2.0 * M_PI / w;
+  if (wavelength < l.original_positions / l.high_freq) return w;
+  if (wavelength > l.original_positions / l.low_freq) return w / l.scale_factor;
+  const double s = (l.original_positions / wavelength - l.low_freq) / (l.high_freq - l.low_freq);
+  return (1.0 - s) * w / l.scale_factor + s * w;
 }
 
 void fill_rope(const Layer& l, hgqa::RopeArgs* r) {
   std::memset(r, 0, sizeof *r);
   r->half = l.half;
   r->rdims = l.rdims;
-  for (int i = 0; i < l.half; ++i)
-    r->freq_over_pi[i] = std::pow((double)l.theta, -2.0 * i / l.rdims) / M_PI;
+  for (int i = 0; i < l.half; ++i) {
+    double w = std::pow((double)l.theta, -2.0 * i / l.rdims);
+    if (l.scale_factor > 1.0) w = llama3_frequency(l, w);
+    r->freq_over_pi[i] = w / M_PI;
+  }
 }
 
 // Largest element count any one buffer may hold; keeps 64-bit offsets exact

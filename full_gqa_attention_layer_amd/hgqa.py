@@ -31,7 +31,9 @@ class HgqaLayer(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("gqa_ratio", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("rope_theta", ctypes.c_float),
                 ("rotary_fraction", ctypes.c_float), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("rope_scaling_factor", ctypes.c_float),
+                ("rope_low_freq_factor", ctypes.c_float), ("rope_high_freq_factor", ctypes.c_float),
+                ("rope_original_max_positions", ctypes.c_int32)]
 
 
 class HgqaError(RuntimeError):
@@ -85,16 +87,19 @@ def _check(rc: int):
 
 def layer(layer_type: int, window: int, num_q_heads: int, gqa_ratio: int, head_dim: int,
           rope_theta: float, rotary_fraction: float = 1.0, softmax_scale: float = 0.0,
-          dtype: int = BF16) -> HgqaLayer:
+          dtype: int = BF16, rope_scaling=()) -> HgqaLayer:
+    """rope_scaling: () for none, or (factor[, low_freq_factor, high_freq_factor,
+    original_max_positions]) of the llama3 frequency scaling (full layers)."""
+    sc = tuple(rope_scaling) + (0.0, 0.0, 0.0, 0)[len(tuple(rope_scaling)):]
     return HgqaLayer(layer_type, window, num_q_heads, gqa_ratio, head_dim, rope_theta,
-                     rotary_fraction, softmax_scale, dtype)
+                     rotary_fraction, softmax_scale, dtype, sc[0], sc[1], sc[2], int(sc[3]))
 
 
 def layer_from_shape(shape, dtype: int = BF16) -> HgqaLayer:
     """Descriptor of a workloads.LayerShape."""
     return layer(shape.layer_type, shape.window, shape.num_q_heads, shape.gqa_ratio,
                  shape.head_dim, shape.rope_theta, shape.rotary_fraction,
-                 shape.softmax_scale, dtype)
+                 shape.softmax_scale, dtype, shape.rope_scaling)
 
 
 def _torch_dtype(L: HgqaLayer):

@@ -29,6 +29,9 @@ class LayerShape:
     rope_theta: float
     rotary_fraction: float = 1.0
     softmax_scale: float = 0.0   # <= 0 means 1/sqrt(head_dim)
+    # () or (factor, low_freq_factor, high_freq_factor, original_max_positions):
+    # llama3 RoPE frequency scaling, full layers only
+    rope_scaling: tuple = ()
 
     @property
     def gqa_ratio(self) -> int:

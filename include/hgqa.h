@@ -83,6 +83,19 @@ enum {
  *                   r == 0 means no rotation.
  *   softmax_scale   > 0 to set the scale; <= 0 selects 1 / sqrt(D)
  *   dtype           HGQA_BF16 or HGQA_FP32
+ *   rope_scaling_factor, rope_low_freq_factor, rope_high_freq_factor,
+ *   rope_original_max_positions
+ *                   long-context RoPE frequency scaling ("rope_type llama3"),
+ *                   which "Step-3.7-Flash-oQ3e" walkthrough 2.3 mounts on full
+ *                   layers only: it is ignored on sliding layers. A factor
+ *                   <= 1 means none (so does a zero-initialised descriptor).
+ *                   With a factor > 1, a frequency w whose wavelength 2 pi / w
+ *                   is below N / high keeps w, one above N / low becomes
+ *                   w / factor, and one in between is blended linearly:
+ *                   s = (N * w / (2 pi) - low) / (high - low),
+ *                   w' = (1 - s) w / factor + s w, N the original context.
+ *                   Fields <= 0 take the defaults low 1, high 4,
+ *                   N 131072; high must exceed low.
  */
 typedef struct {
   int32_t layer_type;
@@ -94,6 +107,10 @@ typedef struct {
   float rotary_fraction;
   float softmax_scale;
   int32_t dtype;
+  float rope_scaling_factor;
+  float rope_low_freq_factor;
+  float rope_high_freq_factor;
+  int32_t rope_original_max_positions;
 } hgqa_layer;
 
 /*

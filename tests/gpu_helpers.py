@@ -24,9 +24,14 @@ def require_gpu():
 
 def spec(shape):
     lt = oracle.SLIDING if shape.layer_type == SLIDING else oracle.FULL
+    sc = tuple(shape.rope_scaling)
+    if sc:   # the library's defaults for parameters left at 0
+        sc = tuple(x if x > 0 else d for x, d in zip(sc + (0.0, 0.0, 0.0)[len(sc) - 1:],
+                                                    (sc[0], 1.0, 4.0, 131072.0)))
     return oracle.LayerSpec(lt, max(shape.window, 1), shape.num_q_heads, shape.num_kv_heads,
                             shape.head_dim, shape.rope_theta, shape.rotary_fraction,
-                            shape.softmax_scale if shape.softmax_scale > 0 else None)
+                            shape.softmax_scale if shape.softmax_scale > 0 else None,
+                            sc if sc and sc[0] > 1.0 else None)
 
 
 def tdtype(dtype):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(hgqa.HgqaLayer) == 36
+    assert ctypes.sizeof(hgqa.HgqaLayer) == 52
     text = open(HEADER).read()
     body = re.search(r"typedef struct \{(.*?)\} hgqa_layer;", text, flags=re.S).group(1)
     fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
@@ -64,6 +64,9 @@ def _call_prefill(lib, L, B=1, T=16, ws=1 << 20, ptr=16):
     (dict(rotary_fraction=8.0 / 128), hgqa.EUNSUPPORTED),      # bf16 needs r % 16 == 0
     (dict(softmax_scale=float("inf")), hgqa.EINVAL),
     (dict(dtype=7), hgqa.EINVAL),
+    (dict(layer_type=0, rope_scaling_factor=2.0, rope_low_freq_factor=4.0,
+          rope_high_freq_factor=2.0), hgqa.EINVAL),             # high must exceed low
+    (dict(rope_scaling_factor=float("nan")), hgqa.EINVAL),
 ])
 def test_invalid_descriptors_are_rejected(lib, kw, code):
     args = dict(layer_type=1, window=64, num_q_heads=8, gqa_ratio=4, head_dim=128,
@@ -72,6 +75,15 @@ def test_invalid_descriptors_are_rejected(lib, kw, code):
     L = hgqa.HgqaLayer(**args)
     assert _call_prefill(lib, L) == code
     assert hgqa.hgqa_last_error() != ""
+
+
+def test_rope_scaling_is_accepted_on_full_and_ignored_on_sliding_layers(lib):
+    # a full layer with scaling and defaults, and a sliding layer carrying
+    # parameters it ignores, both reach the workspace-size check
+    Lf = hgqa.layer(0, 0, 8, 4, 128, 5e6, 0.5, rope_scaling=(2.0,))
+    Ls = hgqa.layer(1, 64, 8, 4, 128, 1e4, 1.0, rope_scaling=(2.0, 4.0, 2.0, 10))
+    for L in (Lf, Ls):
+        assert _call_prefill(lib, L, ws=1) == hgqa.ENOSPACE
 
 
 def test_prefill_argument_checks(lib):

@@ -30,6 +30,7 @@ CASES = [
     (LayerShape(FULL, 0, 8, 2, 64, 1e4, 0.25), hgqa.BF16, 129, 200),
     (LayerShape(SLIDING, 64, 4, 1, 64, 1e4, 1.0), hgqa.FP32, 70, 40),
     (LayerShape(FULL, 0, 6, 2, 128, 5e6, 0.5), hgqa.FP32, 50, 20),
+    (LayerShape(FULL, 0, 8, 1, 128, 1e4, 1.0, 0.0, (2.0, 1.0, 4.0, 256)), hgqa.BF16, 300, 100),
 ]
 B = 2
 

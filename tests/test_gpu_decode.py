@@ -115,7 +115,41 @@ SMALL = [
     (LayerShape(SLIDING, 512, 96, 8, 128, 1e4, 1.0), hgqa.BF16, [100, 512, 2000]),
     (LayerShape(SLIDING, 2048, 32, 2, 128, 5e5, 1.0), hgqa.BF16, [700, 2048, 5000]),
     (LayerShape(FULL, 0, 32, 2, 128, 0.0, 1.0), hgqa.BF16, [3000, 9000]),
+    # llama3 frequency scaling (full layers), short original context
+    (LayerShape(FULL, 0, 8, 2, 128, 1e4, 1.0, 0.0, (2.0, 1.0, 4.0, 256)), hgqa.BF16, [300, 700]),
 ]
+
+
+def test_decode_far_position_with_default_scaling():
+    """The Step full layer with its long-context scaling (factor 2.0, other
+    parameters at the library's defaults): keys appended at positions up to
+    199999, past the original 131072-position context, then a decode there."""
+    require_gpu()
+    shape = LayerShape(FULL, 0, 8, 1, 128, 5e6, 0.5, 0.0, (2.0,))
+    dtype = hgqa.BF16
+    Lq = 200000
+    key = (0, 290, 0)
+    k, v = _kv(shape, 1, Lq, dtype, key)
+    L = hgqa.layer_from_shape(shape, dtype)
+    kc = torch.zeros(1, 1, Lq, 128, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    hgqa.kv_append(L, torch.zeros(1, dtype=torch.int32, device=DEV), Lq, k.to(DEV), v.to(DEV),
+                   kc, vc)
+    # the oracle's cache: slot p holds rope(k_p, p) with the scaled frequencies
+    sp = spec(shape)
+    pos = np.arange(Lq, dtype=np.float64)
+    okc = oracle.rope(f64(k)[0, :, 0], pos, 5e6, 64, sp.frequency_scaling)[None, None]
+    ovc = f64(v)[0, :, 0][None, None]
+    check_cache_per_sequence(kc, vc, okc, ovc, shape, dtype, k, [Lq])
+    unscaled = oracle.rope(f64(k)[0, -1000:, 0], pos[-1000:], 5e6, 64)
+    assert np.abs(unscaled - okc[0, 0, -1000:]).max() > 0.5     # the scaling matters here
+    q = synth.host_normal((1, shape.num_q_heads, shape.head_dim), key + (synth.Q,), torch.bfloat16)
+    g = synth.host_normal((1, shape.num_q_heads), key + (synth.GATE,), torch.bfloat16)
+    seq = torch.tensor([Lq], dtype=torch.int32)
+    out = hgqa.attn_decode(L, q.to(DEV), g.to(DEV), kc, vc, seq.to(DEV), Lq)
+    torch.cuda.synchronize()
+    ref = oracle.decode(f64(q), f64(g), okc, ovc, [Lq], sp)
+    assert_close(out, ref, dtype, "decode at 199999 with llama3 scaling")
 
 
 @pytest.mark.parametrize("idx", range(len(SMALL)))

@@ -51,6 +51,12 @@ SMALL = [
     (LayerShape(SLIDING, 7, 6, 2, 128, 1e4, 0.5), 1, 150, hgqa.FP32),
     (LayerShape(FULL, 0, 4, 1, 64, 1e4, 6.0 / 64), 2, 90, hgqa.FP32),
     (LayerShape(FULL, 0, 2, 2, 128, 0.0, 1.0, 0.3), 1, 70, hgqa.FP32),
+    # llama3 frequency scaling on a full layer, with a short original context so
+    # that all three frequency regimes matter within a few hundred positions
+    (LayerShape(FULL, 0, 8, 1, 128, 1e4, 1.0, 0.0, (2.0, 1.0, 4.0, 256)), 1, 600, hgqa.BF16),
+    (LayerShape(FULL, 0, 4, 2, 128, 5e6, 0.5, 0.0, (3.0, 1.0, 8.0, 64)), 1, 300, hgqa.FP32),
+    # ignored on a sliding layer
+    (LayerShape(SLIDING, 64, 8, 2, 128, 1e4, 1.0, 0.0, (2.0, 1.0, 4.0, 256)), 1, 300, hgqa.BF16),
 ]
 
 
