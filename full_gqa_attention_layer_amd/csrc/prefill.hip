@@ -22,6 +22,8 @@
 // tiles that cross the diagonal or the window edge are masked elementwise.
 #include "device_util.h"
 
+#include <type_traits>
+
 namespace hgqa {
 
 hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s);
@@ -316,7 +318,10 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   const int vd = 16 * dhalf + 4 * (r16 & 3);
 
 
-  for (int it = 0; it < ntiles; ++it) {
+  // One K/V tile. NKB counts the 32-key halves computed: the upper half of a
+  // wave's last tile often holds only keys past all its rows, and is skipped.
+  auto tile = [&](int it, auto nkb_tag) {
+    constexpr int NKB = decltype(nkb_tag)::value;
     const int st = it & 1;
     const int j0 = j_lo + it * kBN;
     if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
@@ -326,7 +331,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     // S^T for two 32-key blocks
     f32x16_t S[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       S[kb] = f32x16_t{};
       const int key = 32 * kb + n;
 #pragma unroll
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       const int base = t_abs - j0 - 4 * g;
       const unsigned wlim = a.sliding ? (unsigned)a.window : 0x80000000u;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -379,7 +384,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     // row sum is taken over the same rounded values.
     u32x4_t pk[4];
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
+    for (int ks4 = 0; ks4 < 2 * NKB; ++ks4) {
       const int kb = ks4 >> 1, hh = ks4 & 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 
     // O^T += V^T P^T, 4 k-steps of 16 keys; V^T comes transposed out of LDS.
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
+    for (int ks4 = 0; ks4 < 2 * NKB; ++ks4) {
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk[ks4]);
       const int k0 = 16 * ks4 + vkey0, k1 = k0 + 8;
 #pragma unroll
@@ -412,7 +417,11 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 
     __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
     __syncthreads();
-  }
+  };
+
+  for (int it = 0; it + 1 < ntiles; ++it) tile(it, std::integral_constant<int, 2>{});
+  if (j_lo + (ntiles - 1) * kBN + 32 > tw_hi) tile(ntiles - 1, std::integral_constant<int, 1>{});
+  else tile(ntiles - 1, std::integral_constant<int, 2>{});
 
   // ---- epilogue: normalise and gate in registers, then turn the O^T
   // fragments into row-major rows in LDS (stage 0 is idle: the loop ended on
