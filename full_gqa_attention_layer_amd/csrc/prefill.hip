@@ -125,6 +125,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int PER_WAVE = CH / kWaves;       // 1 KB loads per wave per operand per tile
   static_assert(CH % kWaves == 0, "each wave moves whole 1 KB pieces");
+  static_assert(2 * PER_WAVE < 16, "tile-0 pieces fit the 4-bit vmcnt field");
   constexpr int NS = D / 16;                  // k-steps of the score product
   constexpr int NDB = D / 32;                 // 32-wide d blocks of the output
   __shared__ PrefillLds<D> sm;
@@ -145,26 +146,49 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   const int b = rest % a.B;
   const int rb = nrb - 1 - rest / a.B;
 
+  // Rows of the block split into (position, head in group). R0 = t0 G + hg0
+  // once; a local row r then needs only the small quotient (hg0 + r) / G,
+  // taken in fp32 as floor((y + 1/2) / G): exact for y < 2^21, because the
+  // half keeps y / G + 1/(2G) at least 1/(2G) away from an integer, far
+  // more than the product's rounding error. Integer division by a runtime G
+  // would cost some 30 VALU instructions per use.
   const int R0 = rb * kRows;
-  const int row = R0 + wave * kRowsPerWave + n;
-  const bool row_ok = row < TG;
-  const int rowc = row_ok ? row : TG - 1;
-  const int t_row = rowc / G;
-  const int h = kvh * G + (rowc - t_row * G);
+  const int t0 = R0 / G, hg0 = R0 - t0 * G;
+  const int nrows = min(kRows, TG - R0);  // rows of this block, >= 1
+  const float inv_g = 1.0f / (float)G, half_inv_g = 0.5f * inv_g;
+  auto split_local = [&](int r, int& dt, int& hg) {
+    const int y = hg0 + r;
+    dt = (int)fmaf((float)y, inv_g, half_inv_g);
+    hg = y - (int)__umul24(dt, G);
+  };
+  auto pos_of_local = [&](int r) {  // position offset from t0 of local row r, uniform r
+    int dt, hg;
+    split_local(r, dt, hg);
+    return __builtin_amdgcn_readfirstlane(dt);
+  };
 
-  const int t_lo = R0 / G;
-  const int t_hi = (min(R0 + kRows, TG) - 1) / G;
-  const int w0 = min(R0 + wave * kRowsPerWave, TG - 1);
-  const int w1 = min(R0 + wave * kRowsPerWave + kRowsPerWave - 1, TG - 1);
+  const int rl = wave * kRowsPerWave + n;
+  const bool row_ok = rl < nrows;
+  int dt_row, hg_row;
+  split_local(min(rl, nrows - 1), dt_row, hg_row);
+  const int t_row = t0 + dt_row;
+  const int h = kvh * G + hg_row;
+
+  const int t_lo = t0;
+  const int t_hi = t0 + pos_of_local(nrows - 1);
   // Masks and key ranges use absolute positions: row t of this call sits at
   // p0 + t, and so does key t of this call.
   const int p0 = kCache ? a.p0 : 0;
-  const int tw_lo = p0 + w0 / G, tw_hi = p0 + w1 / G;
+  const int tw_lo = p0 + t0 + pos_of_local(min(wave * kRowsPerWave, nrows - 1));
+  const int tw_hi = p0 + t0 + pos_of_local(min(wave * kRowsPerWave + kRowsPerWave - 1, nrows - 1));
   const int t_abs = p0 + t_row;
 
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kr = static_cast<const uint16_t*>(a.k_rot);
   const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v);
+  // Memory row of (position t0, first head of the group); a row of the block
+  // sits dt Hq + hg rows further on.
+  const size_t blk_row = (size_t)(b * T + t0) * Hq + kvh * G;
 
   // ---- key range of the workgroup (absolute positions)
   const int j_lo = a.sliding ? max(0, p0 + t_lo - a.window + 1) : 0;
@@ -181,35 +205,33 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // the causal mask hides (their probabilities are exactly 0). In a chunk,
   // keys before p0 come from the cache: slot j, or j mod cap in a ring.
   auto load_tile = [&](int j0, int st) {
+    const int kmax = j_last - j0;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int I = wave * PER_WAVE + i;
       const int P = 64 * I + lane;
       const int key = P / CH, pos = P % CH;
-      const int j = min(j0 + key, j_last);
+      const int kk = min(key, kmax);
       const uint16_t* ksrc;
       const uint16_t* vsrc;
-      if (kCache && j < p0) {
-        const size_t off = cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
-        ksrc = static_cast<const uint16_t*>(a.k_cache) + off + 8 * (pos ^ Swz<D>::k(key));
-        vsrc = static_cast<const uint16_t*>(a.v_cache) + off + 8 * (pos ^ Swz<D>::v(key));
+      if constexpr (kCache) {
+        const int j = j0 + kk;
+        if (j < p0) {
+          const size_t off = cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
+          ksrc = static_cast<const uint16_t*>(a.k_cache) + off + 8 * (pos ^ Swz<D>::k(key));
+          vsrc = static_cast<const uint16_t*>(a.v_cache) + off + 8 * (pos ^ Swz<D>::v(key));
+        } else {
+          ksrc = kbase + (size_t)(j - p0) * D + 8 * (pos ^ Swz<D>::k(key));
+          vsrc = vbase + (size_t)(j - p0) * vstride + 8 * (pos ^ Swz<D>::v(key));
+        }
       } else {
-        ksrc = kbase + (size_t)(j - p0) * D + 8 * (pos ^ Swz<D>::k(key));
-        vsrc = vbase + (size_t)(j - p0) * vstride + 8 * (pos ^ Swz<D>::v(key));
+        // uniform tile bases, 32-bit lane offsets
+        ksrc = kbase + (size_t)j0 * D + (uint32_t)(kk * D + 8 * (pos ^ Swz<D>::k(key)));
+        vsrc = vbase + (size_t)j0 * vstride + (uint32_t)(__umul24(kk, (unsigned)vstride) + 8 * (pos ^ Swz<D>::v(key)));
       }
       __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
     }
-  };
-
-  // The first K/V tile starts moving before anything else.
-  if (ntiles > 0) load_tile(j_lo, 0);
-
-  // Memory row R of the block (clamped to the last row): its Q / output row.
-  auto row_offset = [&](int R) -> size_t {
-    const int Rc = min(R, TG - 1);
-    const int t = Rc / G;
-    return ((size_t)(b * T + t) * Hq + kvh * G + (Rc - t * G)) * D;
   };
 
   // ---- the block's Q rows go to stage 1 (idle until the loop starts), four
@@ -223,7 +245,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       const int I = wave * Q_PIECES + i;
       const int Pc = 64 * I + lane;
       const int r = Pc / CH, pos = Pc % CH;
-      const uint16_t* src = qp + row_offset(R0 + r) + 8 * (pos ^ Swz<D>::k(r));
+      int dt, hg;
+      split_local(min(r, nrows - 1), dt, hg);
+      const uint16_t* src = qp + blk_row * D + (uint32_t)((__umul24(dt, Hq) + hg) * D + 8 * (pos ^ Swz<D>::k(r)));
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)&qs[512 * I], 16, 0, 0);
     }
   }
@@ -247,13 +271,18 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // The gate logit is needed only at the end; fetch it now so its latency
   // hides behind the tile loop.
   const float gate_logit =
-      bf16_to_f32(static_cast<const uint16_t*>(a.gate)[(size_t)(b * T + t_row) * Hq + h]);
+      bf16_to_f32(static_cast<const uint16_t*>(a.gate)[blk_row + (uint32_t)(__umul24(dt_row, Hq) + hg_row)]);
 
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // tile 0, the Q rows and the cos/sin rows have landed
+  // Tile 0 moves while Q is rotated. Vector-memory counts retire in issue
+  // order, so waiting until this wave's 2 PER_WAVE tile-0 pieces are the only
+  // ones left means its Q and cos/sin pieces have landed. (ntiles >= 1: the
+  // diagonal key is always visible.)
+  load_tile(j_lo, 0);
+  __builtin_amdgcn_s_waitcnt((2 * PER_WAVE) | (7 << 4) | (15 << 8));  // vmcnt(2 PER_WAVE)
+  __builtin_amdgcn_s_barrier();  // every wave's Q and cos/sin pieces have landed
 
   // ---- Q^T fragments: lane holds row n, dims 16s+8g..+7, rotated below.
-  const uint16_t* qrow = qp + ((size_t)(b * T + t_row) * Hq + h) * D;
+  const uint16_t* qrow = qp + blk_row * D + (uint32_t)((__umul24(dt_row, Hq) + hg_row) * D);
   u32x4_t qraw[NS];
   {
     const int r = wave * kRowsPerWave + n;
@@ -269,8 +298,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     for (int s = 0; s < NS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qraw[s]);
   } else if (half % 16 == 0) {
     // The RoPE partner of every chunk sits in this lane, half/16 chunks away.
-    const int tl = t_row - t_lo;
-    const float2* csl = sm.cs + tl * half;
+    const float2* csl = sm.cs + dt_row * half;
     const float2* csg = a.cs_table + (size_t)t_row * half;
     switch (half / 16) {
 #define HGQA_ROPE_CASE(H)                                 \
@@ -301,7 +329,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       qf[s] = pack8(x);
     }
   }
-  __syncthreads();  // Q and the cos/sin rows are read before stage 1 is refilled
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // tile 0 has landed; Q and the cos/sin rows are read before stage 1 is refilled
 
   f32x16_t O[NDB];
 #pragma unroll
@@ -445,10 +474,12 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   for (int i = 0; i < O_PIECES; ++i) {
     const int Pc = 64 * i + lane;
     const int r = Pc / CH, pos = Pc % CH;  // row of the wave, LDS position
-    const int R = R0 + wave * kRowsPerWave + r;
+    const int rb_local = wave * kRowsPerWave + r;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ow + r * D + 8 * pos);
-    if (R < TG)
-      *reinterpret_cast<u32x4_t*>(op + row_offset(R) + 8 * (pos ^ Swz<D>::k(r))) = v;
+    int dt, hg;
+    split_local(rb_local, dt, hg);
+    if (rb_local < nrows)
+      *reinterpret_cast<u32x4_t*>(op + blk_row * D + (uint32_t)((__umul24(dt, Hq) + hg) * D + 8 * (pos ^ Swz<D>::k(r)))) = v;
   }
 }
 
