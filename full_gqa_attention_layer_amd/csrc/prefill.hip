@@ -104,6 +104,15 @@ __device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t
   }
 }
 
+// Buffer descriptors give a tile's copies a uniform base, so the fixed 32-bit
+// lane offsets need no per-tile vector arithmetic. bytes bounds the copy.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void_t* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
 constexpr int kCsFloat2 = 1024;  // cos/sin rows of one row block: 8 KB
 
 // One stage holds a K tile and a V tile. Stage 1 first holds the block's Q
@@ -204,33 +213,51 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // both tiles. Keys past the end re-read the last key: finite values that
   // the causal mask hides (their probabilities are exactly 0). In a chunk,
   // keys before p0 come from the cache: slot j, or j mod cap in a ring.
+  // Byte offsets of this wave's pieces inside a tile. A tile that ends at or
+  // before the last key is then a uniform base plus these fixed lane offsets,
+  // with no per-tile address arithmetic.
+  uint32_t koff[PER_WAVE], voff[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) {
+    const int P = 64 * (wave * PER_WAVE + i) + lane;
+    const int key = P / CH, pos = P % CH;
+    koff[i] = 2u * (uint32_t)(key * D + 8 * (pos ^ Swz<D>::k(key)));
+    voff[i] = 2u * (__umul24(key, (unsigned)vstride) + 8 * (pos ^ Swz<D>::v(key)));
+  }
   auto load_tile = [&](int j0, int st) {
     const int kmax = j_last - j0;
+    const char* kt = reinterpret_cast<const char*>(kbase + (size_t)(j0 - p0) * D);
+    const char* vt = reinterpret_cast<const char*>(vbase + (size_t)(j0 - p0) * vstride);
+    auto issue = [&](int I, const void* ksrc, const void* vsrc) {
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
+    };
+    if (!kCache && kmax >= kBN - 1) {
+      const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kt, kBN * D * 2);
+      const __amdgpu_buffer_rsrc_t vres = tile_rsrc(vt, (uint32_t)(((kBN - 1) * vstride + D) * 2));
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int I = wave * PER_WAVE + i;
+        copy16_to_lds(kres, (lds_void_t*)&sm.st[st].k[512 * I], koff[i]);
+        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], voff[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int I = wave * PER_WAVE + i;
       const int P = 64 * I + lane;
       const int key = P / CH, pos = P % CH;
       const int kk = min(key, kmax);
-      const uint16_t* ksrc;
-      const uint16_t* vsrc;
-      if constexpr (kCache) {
-        const int j = j0 + kk;
-        if (j < p0) {
-          const size_t off = cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
-          ksrc = static_cast<const uint16_t*>(a.k_cache) + off + 8 * (pos ^ Swz<D>::k(key));
-          vsrc = static_cast<const uint16_t*>(a.v_cache) + off + 8 * (pos ^ Swz<D>::v(key));
-        } else {
-          ksrc = kbase + (size_t)(j - p0) * D + 8 * (pos ^ Swz<D>::k(key));
-          vsrc = vbase + (size_t)(j - p0) * vstride + 8 * (pos ^ Swz<D>::v(key));
-        }
+      const int j = j0 + kk;
+      if (kCache && j < p0) {
+        const size_t off = cache_head + (size_t)(a.ring ? j % a.cap : j) * D;
+        issue(I, static_cast<const uint16_t*>(a.k_cache) + off + 8 * (pos ^ Swz<D>::k(key)),
+              static_cast<const uint16_t*>(a.v_cache) + off + 8 * (pos ^ Swz<D>::v(key)));
       } else {
-        // uniform tile bases, 32-bit lane offsets
-        ksrc = kbase + (size_t)j0 * D + (uint32_t)(kk * D + 8 * (pos ^ Swz<D>::k(key)));
-        vsrc = vbase + (size_t)j0 * vstride + (uint32_t)(__umul24(kk, (unsigned)vstride) + 8 * (pos ^ Swz<D>::v(key)));
+        issue(I, kbase + (size_t)(j - p0) * D + 8 * (pos ^ Swz<D>::k(key)),
+              vbase + (size_t)(j - p0) * vstride + 8 * (pos ^ Swz<D>::v(key)));
       }
-      __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
     }
   };
 
