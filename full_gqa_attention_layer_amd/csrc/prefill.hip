@@ -376,8 +376,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 
   // One K/V tile. NKB counts the 32-key halves computed: the upper half of a
   // wave's last tile often holds only keys past all its rows, and is skipped.
-  auto tile = [&](int it, auto nkb_tag) {
+  auto tile = [&](int it, auto nkb_tag, auto first_tag) {
     constexpr int NKB = decltype(nkb_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const int st = it & 1;
     const int j0 = j_lo + it * kBN;
     if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
@@ -427,7 +428,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     // reference.
     const float m_cand = mx * sc;
     const bool need = m_cand > m_run + 8.0f;
-    if (__any(need)) {
+    if (FIRST) {
+      m_run = need ? m_cand : m_run;  // O and l are still zero: nothing to rescale
+    } else if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.0f;
       l_run *= alpha;
 #pragma unroll
@@ -475,9 +478,16 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     __syncthreads();
   };
 
-  for (int it = 0; it + 1 < ntiles; ++it) tile(it, std::integral_constant<int, 2>{});
-  if (j_lo + (ntiles - 1) * kBN + 32 > tw_hi) tile(ntiles - 1, std::integral_constant<int, 1>{});
-  else tile(ntiles - 1, std::integral_constant<int, 2>{});
+  // The first tile (when it is not also the last) is its own copy: it sets
+  // the softmax reference without rescaling the still-zero output.
+  using Later = std::integral_constant<bool, false>;
+  using First = std::integral_constant<bool, true>;
+  using Full = std::integral_constant<int, 2>;
+  using Half = std::integral_constant<int, 1>;
+  if (ntiles > 1) tile(0, Full{}, First{});
+  for (int it = 1; it + 1 < ntiles; ++it) tile(it, Full{}, Later{});
+  if (j_lo + (ntiles - 1) * kBN + 32 > tw_hi) tile(ntiles - 1, Half{}, Later{});
+  else tile(ntiles - 1, Full{}, Later{});
 
   // ---- epilogue: normalise and gate in registers, then turn the O^T
   // fragments into row-major rows in LDS (stage 0 is idle: the loop ended on
