@@ -31,8 +31,10 @@ def sources():
 
 
 def command(out: str = LIB_PATH, extra=()):
+    # -z defs: an unresolved symbol (for instance a kernel whose host stub the
+    # compiler did not emit) fails the link instead of the first dlopen.
     return ([hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
-             "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS + list(extra)
+             "-Wl,-z,defs", "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS + list(extra)
             + sources() + ["-o", out])
 
 

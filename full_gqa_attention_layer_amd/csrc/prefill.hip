@@ -17,7 +17,9 @@
 // so the softmax probabilities leave the score accumulator already in the
 // B-operand layout of the second product. V is stored transposed in LDS with
 // its keys permuted to match. K arrives pre-rotated from the pre-pass; Q is
-// rotated while it is loaded, from the pre-pass's cos/sin table. Only tiles
+// rotated while it is loaded, from the pre-pass's cos/sin table, and carries
+// the softmax scale in log2 units; the score accumulators start from minus
+// the row's softmax reference, so exp2 applies to them directly. Only tiles
 // that hold a visible key are visited (sliding layers cost O(T*W)), and only
 // tiles that cross the diagonal or the window edge are masked elementwise.
 #include "device_util.h"
@@ -84,10 +86,11 @@ __device__ __forceinline__ void rotate8(float (&x)[8], u32x4_t praw, const float
 
 // Rotates a lane's Q chunks (chunk s = dims 16s+8g..+7) when r/2 = 16 H16:
 // chunk s < H16 pairs with chunk s + H16 of the same lane; chunks up to
-// 2 H16 rotate, the rest pass through.
+// 2 H16 rotate, the rest pass through. Every value is then multiplied by
+// qscale before its one rounding to bf16.
 template <int NS, int H16>
 __device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t (&qf)[NS], int g,
-                                              const float2* cs) {
+                                              const float2* cs, float qscale) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     float x[8];
@@ -100,6 +103,8 @@ __device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t
         rotate8(x, raw[sp < NS ? sp : 0], cs + i0, first ? -1.0f : 1.0f);
       }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= qscale;
     qf[s] = pack8(x);
   }
 }
@@ -109,8 +114,9 @@ __device__ __forceinline__ void rope_q_inlane(const u32x4_t (&raw)[NS], bf16x8_t
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void_t* dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void_t* dst, uint32_t voff,
+                                              uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
 constexpr int kCsFloat2 = 1024;  // cos/sin rows of one row block: 8 KB
@@ -216,14 +222,18 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // Byte offsets of this wave's pieces inside a tile. A tile that ends at or
   // before the last key is then a uniform base plus these fixed lane offsets,
   // with no per-tile address arithmetic.
-  uint32_t koff[PER_WAVE], voff[PER_WAVE];
+  // V's swizzle repeats every KPP keys (the keys of one piece), so its
+  // pieces sit a fixed stride apart and one lane offset serves them all.
+  constexpr int KPP = 64 / CH;  // keys per 1 KB piece
+  uint32_t koff[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) {
     const int P = 64 * (wave * PER_WAVE + i) + lane;
     const int key = P / CH, pos = P % CH;
     koff[i] = 2u * (uint32_t)(key * D + 8 * (pos ^ Swz<D>::k(key)));
-    voff[i] = 2u * (__umul24(key, (unsigned)vstride) + 8 * (pos ^ Swz<D>::v(key)));
   }
+  const int key_l = wave * PER_WAVE * KPP + lane / CH;  // the lane's key in the wave's first piece
+  const uint32_t voff = 2u * (__umul24(key_l, (unsigned)vstride) + 8 * ((lane % CH) ^ Swz<D>::v(key_l)));
   auto load_tile = [&](int j0, int st) {
     const int kmax = j_last - j0;
     const char* kt = reinterpret_cast<const char*>(kbase + (size_t)(j0 - p0) * D);
@@ -238,8 +248,9 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int I = wave * PER_WAVE + i;
-        copy16_to_lds(kres, (lds_void_t*)&sm.st[st].k[512 * I], koff[i]);
-        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], voff[i]);
+        copy16_to_lds(kres, (lds_void_t*)&sm.st[st].k[512 * I], koff[i], 0u);
+        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], voff,
+                      (uint32_t)(i * KPP * vstride * 2));
       }
       return;
     }
@@ -319,10 +330,19 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
       qraw[s] = *reinterpret_cast<const u32x4_t*>(qs + 8 * ((2 * s + g) ^ Swz<D>::k(r)));
   }
 
+  // q is rotated and multiplied by scale * log2(e) before its one rounding to
+  // bf16, so scores come out of the MFMA in log2 units.
+  const float sc = a.scale * kLog2e;
   bf16x8_t qf[NS];
   if (half == 0) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) qf[s] = __builtin_bit_cast(bf16x8_t, qraw[s]);
+    for (int s = 0; s < NS; ++s) {
+      float x[8];
+      unpack8(qraw[s], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= sc;
+      qf[s] = pack8(x);
+    }
   } else if (half % 16 == 0) {
     // The RoPE partner of every chunk sits in this lane, half/16 chunks away.
     const float2* csl = sm.cs + dt_row * half;
@@ -330,8 +350,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     switch (half / 16) {
 #define HGQA_ROPE_CASE(H)                                 \
   case H:                                                 \
-    if (cs_lds) rope_q_inlane<NS, H>(qraw, qf, g, csl);   \
-    else rope_q_inlane<NS, H>(qraw, qf, g, csg);          \
+    if (cs_lds) rope_q_inlane<NS, H>(qraw, qf, g, csl, sc);   \
+    else rope_q_inlane<NS, H>(qraw, qf, g, csg, sc);          \
     break;
       HGQA_ROPE_CASE(1)
       HGQA_ROPE_CASE(2)
@@ -353,6 +373,8 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
         u32x4_t praw = *reinterpret_cast<const u32x4_t*>(qrow + (first ? d0 + half : d0 - half));
         rotate8(x, praw, csrow + i0, first ? -1.0f : 1.0f);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= sc;
       qf[s] = pack8(x);
     }
   }
@@ -363,7 +385,11 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
 #pragma unroll
   for (int i = 0; i < NDB; ++i) O[i] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.0f;
-  const float sc = a.scale * kLog2e;
+  // Scores are kept relative to m_use (m_run, or 0 while a row has seen no
+  // key) in log2 units: q carries scale * log2(e), and the score products
+  // start from -m_use instead of zero, so the exponent needs no arithmetic.
+  float m_use = 0.0f;
+  f32x16_t negm = {};
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // V^T operand supplier addresses for ds_read_b64_tr_b16: lane r of each
@@ -389,7 +415,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     f32x16_t S[2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      S[kb] = f32x16_t{};
+      S[kb] = FIRST ? f32x16_t{} : negm;
       const int key = 32 * kb + n;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
@@ -425,30 +451,35 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
     // m_run is a per-row reference, not the exact running maximum: it moves
     // only when a score exceeds it by more than 2^8, so probabilities stay
     // below 256 and the output is rescaled rarely; O / l is exact for any
-    // reference.
-    const float m_cand = mx * sc;
+    // reference. S already holds score - m_use in log2 units (the first tile
+    // holds plain scores); when the reference moves, S shifts with it.
+    const float m_cand = FIRST ? mx : mx + m_use;
     const bool need = m_cand > m_run + 8.0f;
-    if (FIRST) {
-      m_run = need ? m_cand : m_run;  // O and l are still zero: nothing to rescale
-    } else if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.0f;
-      l_run *= alpha;
+    if (FIRST || __any(need)) {
+      if (!FIRST) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_cand) : 1.0f;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+        for (int i = 0; i < NDB; ++i) O[i] *= alpha;
+      }
+      const float shift = need ? m_cand - (FIRST ? 0.0f : m_use) : 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) S[kb] -= shift;
       m_run = need ? m_cand : m_run;
+      m_use = (m_run == -INFINITY) ? 0.0f : m_run;
+      negm = f32x16_t{} - m_use;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.0f : m_run;
 
-    // P = exp2(S*sc - m), packed to bf16 in the B-operand order of PV; the
-    // row sum is taken over the same rounded values.
+    // P = exp2(S), packed to bf16 in the B-operand order of PV; the row sum
+    // is taken over the same rounded values.
     u32x4_t pk[4];
 #pragma unroll
     for (int ks4 = 0; ks4 < 2 * NKB; ++ks4) {
       const int kb = ks4 >> 1, hh = ks4 & 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pa = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e], sc, -m_use));
-        const float pb = __builtin_amdgcn_exp2f(fmaf(S[kb][8 * hh + 2 * e + 1], sc, -m_use));
+        const float pa = __builtin_amdgcn_exp2f(S[kb][8 * hh + 2 * e]);
+        const float pb = __builtin_amdgcn_exp2f(S[kb][8 * hh + 2 * e + 1]);
         const bf16x2_t pv = {(__bf16)pa, (__bf16)pb};
         pk[ks4][e] = __builtin_bit_cast(uint32_t, pv);
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pv, ones, l_run, false);

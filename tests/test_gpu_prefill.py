@@ -74,9 +74,11 @@ def test_peaky_scores():
     """Queries scaled by 8 make the softmax nearly one-hot and the scores 8x
     larger, so the bf16 rounding of the rotated q and k (the MFMA inputs)
     moves the scores 8x further than at unit scale. Two checks:
-      * against the oracle fed the same rounded rotated q and k (base 0 on
-        pre-rotated inputs): the usual bf16 bar, which isolates everything
-        else the kernel does;
+      * against the oracle fed the kernel's own MFMA inputs (base 0 on
+        pre-rotated inputs): k rotated and rounded to bf16, and q rotated,
+        multiplied by c = scale * log2(e) (the kernel takes scores in log2
+        units), rounded to bf16 and divided by c again; the usual bf16 bar,
+        which isolates everything else the kernel does;
       * against the plain oracle: max-abs within 8 x the usual bar (the score
         error, and with it the output error, grows linearly with q's scale),
         mean-abs within the usual bar."""
@@ -87,7 +89,8 @@ def test_peaky_scores():
     q = (q.float() * s).to(torch.bfloat16)
     out = run_prefill(shape, hgqa.BF16, q, k, v, g)
     pos = np.arange(400, dtype=np.float64)[None, :, None]
-    qr = oracle.round_bf16(oracle.rope(f64(q), pos, 1e4, 128))
+    c = np.log2(np.e) / np.sqrt(128.0)
+    qr = oracle.round_bf16(oracle.rope(f64(q), pos, 1e4, 128) * c) / c
     kr = oracle.round_bf16(oracle.rope(f64(k), pos, 1e4, 128))
     unrotated = LayerShape(SLIDING, 64, 16, 2, 128, 0.0, 1.0)
     ref_r = oracle.prefill(qr, kr, f64(v), f64(g), spec(unrotated))
