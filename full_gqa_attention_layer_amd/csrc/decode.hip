@@ -125,7 +125,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
-  // The first chunk starts moving before q is rotated.
+  // The first chunk starts moving, then q (with each chunk's RoPE partner)
+  // and the RoPE frequencies are requested right behind it, so one memory
+  // round trip brings all three. (The compiler waits for every outstanding
+  // load before a register loaded next to an HBM -> LDS copy is used.)
   constexpr int STEP = kChunk * kDecWaves;
   u32x4_t kfa[2][NS], kfb[2][NS];
   uint16_t* va_buf = sm.u.v[wave][0];
@@ -133,42 +136,51 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   int key0 = k_begin + kChunk * wave;
   if (key0 < k_end) issue(key0, kfa, va_buf);
 
-  // ---- rotate q at position L-1; lane holds head n16, dims 32s+8g..+7
   const int half = a.rope.half, rdims = a.rope.rdims;
-  for (int i = tid; i < half; i += kDecThreads) sm.cs[i] = rope_cos_sin(L - 1, a.rope.freq_over_pi[i]);
-  __syncthreads();
-  bf16x8_t qf[NS];
+  static_assert(kMaxHalfRotary <= kDecThreads, "one frequency per thread");
+  const double freq = tid < half ? a.rope.freq_over_pi[tid] : 0.0;
+  const bool hv = n16 < G;
+  u32x4_t qraw[NS], qpart[NS];
   {
-    const bool hv = n16 < G;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((size_t)b * a.Hq + kvh * G + (hv ? n16 : 0)) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int d0 = 32 * s + 8 * g;
-      u32x4_t raw = *reinterpret_cast<const u32x4_t*>(qrow + d0);
-      float x[8];
+      const int dp = d0 < half ? d0 + half : (d0 < rdims ? d0 - half : d0);
+      qraw[s] = *reinterpret_cast<const u32x4_t*>(qrow + d0);
+      qpart[s] = *reinterpret_cast<const u32x4_t*>(qrow + dp);
+    }
+  }
+
+  // ---- rotate q at position L-1; lane holds head n16, dims 32s+8g..+7
+  if (tid < half) sm.cs[tid] = rope_cos_sin(L - 1, freq);
+  __syncthreads();
+  bf16x8_t qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int d0 = 32 * s + 8 * g;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(qraw[s][e]);
+      x[2 * e + 1] = bf16_hi(qraw[s][e]);
+    }
+    if (d0 < rdims) {
+      const bool first = d0 < half;
+      const int i0 = first ? d0 : d0 - half;
+      const float sgn = first ? -1.0f : 1.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[2 * e] = bf16_lo(raw[e]);
-        x[2 * e + 1] = bf16_hi(raw[e]);
+        float2 c0 = sm.cs[i0 + 2 * e], c1 = sm.cs[i0 + 2 * e + 1];
+        x[2 * e] = fmaf(x[2 * e], c0.x, sgn * bf16_lo(qpart[s][e]) * c0.y);
+        x[2 * e + 1] = fmaf(x[2 * e + 1], c1.x, sgn * bf16_hi(qpart[s][e]) * c1.y);
       }
-      if (d0 < rdims) {
-        const bool first = d0 < half;
-        const int i0 = first ? d0 : d0 - half;
-        const float sgn = first ? -1.0f : 1.0f;
-        u32x4_t praw = *reinterpret_cast<const u32x4_t*>(qrow + (first ? d0 + half : d0 - half));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float2 c0 = sm.cs[i0 + 2 * e], c1 = sm.cs[i0 + 2 * e + 1];
-          x[2 * e] = fmaf(x[2 * e], c0.x, sgn * bf16_lo(praw[e]) * c0.y);
-          x[2 * e + 1] = fmaf(x[2 * e + 1], c1.x, sgn * bf16_hi(praw[e]) * c1.y);
-        }
-      }
-      u32x4_t packed;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) packed[e] = hv ? pack_bf16x2(x[2 * e], x[2 * e + 1]) : 0u;
-      qf[s] = __builtin_bit_cast(bf16x8_t, packed);
     }
+    u32x4_t packed;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) packed[e] = hv ? pack_bf16x2(x[2 * e], x[2 * e + 1]) : 0u;
+    qf[s] = __builtin_bit_cast(bf16x8_t, packed);
   }
 
   // V^T operand supplier addresses for ds_read_b64_tr_b16: lane r of each
