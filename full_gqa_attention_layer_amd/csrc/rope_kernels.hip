@@ -130,11 +130,16 @@ hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s) {
   return hipGetLastError();
 }
 
-// grid (n_new, B), block 256. One block per new token.
+// grid (tokens, B), block 256. One block per new token that reaches the
+// cache: all n_new of them for a full cache, the last min(n_new, W) for a
+// ring (earlier ones would be overwritten within this call).
+__host__ __device__ inline int append_first_token(const AppendArgs& a) {
+  return a.sliding && a.n_new > a.window ? a.n_new - a.window : 0;
+}
 template <typename T>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   __shared__ float2 cs[kMaxHalfRotary];
-  const int n = blockIdx.x, b = blockIdx.y;
+  const int n = blockIdx.x + append_first_token(a), b = blockIdx.y;
   const int start = a.start_pos ? a.start_pos[b] : a.start_uniform;
   const int p = start + n;
   if (p < 0) return;
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, Elem e, hipStream_t s) {
-  dim3 grid(a.n_new, a.B);
+  dim3 grid(a.n_new - append_first_token(a), a.B);
   if (e == Elem::BF16)
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else
