@@ -24,6 +24,7 @@
 // tiles that cross the diagonal or the window edge are masked elementwise.
 #include "device_util.h"
 
+#include <cstdlib>
 #include <type_traits>
 
 namespace hgqa {
@@ -31,9 +32,7 @@ namespace hgqa {
 hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s);
 
 // ------------------------------------------------------------------ bf16
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kRows = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kBN = 64;                       // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -121,29 +120,36 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void
 
 constexpr int kCsFloat2 = 1024;  // cos/sin rows of one row block: 8 KB
 
-// One stage holds a K tile and a V tile. Stage 1 first holds the block's Q
-// rows (kRows x D bf16 = kBN x 2D), stage 0 finally the output rows.
+// One stage holds a K tile and a V tile. With 4 waves (128 rows), stage 1
+// first holds the block's Q rows (128 x D bf16 = kBN x 2D) and stage 0
+// finally the output rows; with 8 waves (256 rows, one workgroup per CU) a
+// separate area holds first Q, then the output.
 template <int D>
 struct PrefillStage {
   uint16_t k[kBN * D];
   uint16_t v[kBN * D];
 };
-template <int D>
+template <int D, int KW>
 struct PrefillLds {
   PrefillStage<D> st[2];
-  float2 cs[kCsFloat2];
+  uint16_t qo[KW > 4 ? KW * kRowsPerWave * D : 8];
+  float2 cs[KW > 4 ? 2 * kCsFloat2 : kCsFloat2];
 };
 
 // kCache: chunked prefill, keys before position p0 come from the cache.
-template <int D, bool kCache>
-__global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(PrefillArgs a) {
+// KW: waves per workgroup (4: two workgroups per CU; 8: one, every K/V tile
+// serving twice the rows).
+template <int D, bool kCache, int KW>
+__global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int kWaves = KW;
+  constexpr int kRows = kWaves * kRowsPerWave;  // query rows per workgroup
   constexpr int CH = D / 8;                   // 16-byte chunks per row
   constexpr int PER_WAVE = CH / kWaves;       // 1 KB loads per wave per operand per tile
   static_assert(CH % kWaves == 0, "each wave moves whole 1 KB pieces");
   static_assert(2 * PER_WAVE < 16, "tile-0 pieces fit the 4-bit vmcnt field");
   constexpr int NS = D / 16;                  // k-steps of the score product
   constexpr int NDB = D / 32;                 // 32-wide d blocks of the output
-  __shared__ PrefillLds<D> sm;
+  __shared__ PrefillLds<D, KW> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -277,7 +283,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // the layout K tiles use, so the fragment reads below are conflict-free.
   {
     constexpr int Q_PIECES = kRows * D * 2 / 1024 / kWaves;
-    uint16_t* qs = reinterpret_cast<uint16_t*>(&sm.st[1]);
+    uint16_t* qs = KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[1]);
 #pragma unroll
     for (int i = 0; i < Q_PIECES; ++i) {
       const int I = wave * Q_PIECES + i;
@@ -324,7 +330,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   u32x4_t qraw[NS];
   {
     const int r = wave * kRowsPerWave + n;
-    const uint16_t* qs = reinterpret_cast<const uint16_t*>(&sm.st[1]) + r * D;
+    const uint16_t* qs = (KW > 4 ? sm.qo : reinterpret_cast<const uint16_t*>(&sm.st[1])) + r * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qraw[s] = *reinterpret_cast<const u32x4_t*>(qs + 8 * ((2 * s + g) ^ Swz<D>::k(r)));
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(kWaves * 64, 8 / kWaves) void prefill_bf16_kernel(P
   // a barrier with no load in flight) so that the stores write whole rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = row_ok ? sigmoidf_dev(gate_logit) / l_tot : 0.0f;
-  uint16_t* ow = reinterpret_cast<uint16_t*>(&sm.st[0]) + wave * (kRowsPerWave * D);  // this wave's rows
+  uint16_t* ow = (KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[0])) + wave * (kRowsPerWave * D);  // this wave's rows
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -625,6 +631,21 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   if (lane + 64 < D) o[lane + 64] = o1 * f;
 }
 
+// Waves per workgroup. 8 (one workgroup per CU, each K/V tile copied once
+// for 256 rows) when a block visits many tiles: full layers and windows of
+// 1024 keys or more (measured: full layers 4-5% faster, W = 2048 3-4%). 4
+// for short windows, where a workgroup's fixed costs weigh more and two
+// workgroups per CU hide them (W = 512: 8 waves is 9% slower). D = 128
+// without a cache only. HGQA_PREFILL_WAVES=4|8 overrides (tuning only).
+static int prefill_waves(const PrefillArgs& a) {
+  int kw = (a.D == 128 && a.k_cache == nullptr && (!a.sliding || a.window >= 1024)) ? 8 : 4;
+  if (const char* env = getenv("HGQA_PREFILL_WAVES")) {
+    const int v = atoi(env);
+    if ((v == 4 || v == 8) && a.D == 128 && a.k_cache == nullptr) kw = v;
+  }
+  return kw;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   hipError_t err = launch_prefill_prepass(a, e, s);
   if (err != hipSuccess) return err;
@@ -634,16 +655,18 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
     return hipGetLastError();
   }
   const long long TG = (long long)a.T * a.G;
-  const long long nrb = (TG + kRows - 1) / kRows;
-  const long long blocks = nrb * a.B * a.Hkv;
-  const dim3 grid((unsigned)blocks), block(kWaves * 64);
   const bool cache = a.k_cache != nullptr;
+  const int kw = prefill_waves(a);
+  const long long rows = (long long)kw * kRowsPerWave;
+  const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv;
+  const dim3 grid((unsigned)blocks), block(kw * 64);
   if (a.D == 128) {
-    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 4>), grid, block, 0, s, a);
+    else if (kw == 8) hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 4>), grid, block, 0, s, a);
   } else {
-    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, 4>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

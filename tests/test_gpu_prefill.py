@@ -70,6 +70,29 @@ def test_prefill_small_shapes_all_rows(idx):
     assert_close(out, ref, dtype, f"small[{idx}] {shape} B{B} T{T}")
 
 
+# Both workgroup shapes of the bf16 kernel (4 waves / 128 rows and 8 waves /
+# 256 rows) on each kind of layer, whatever the launcher would pick.
+WAVE_CASES = [
+    (LayerShape(SLIDING, 64, 8, 2, 128, 1e4, 1.0), 1, 300),
+    (LayerShape(FULL, 0, 12, 1, 128, 5e6, 0.5), 2, 517),
+    (LayerShape(SLIDING, 1024, 8, 1, 128, 5e5, 1.0), 1, 1200),
+    (LayerShape(FULL, 0, 24, 2, 128, 1e4, 1.0), 1, 1),
+    (LayerShape(FULL, 0, 16, 1, 128, 0.0, 1.0), 1, 333),
+]
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("idx", range(len(WAVE_CASES)))
+def test_prefill_both_workgroup_shapes(idx, waves, monkeypatch):
+    require_gpu()
+    monkeypatch.setenv("HGQA_PREFILL_WAVES", str(waves))
+    shape, B, T = WAVE_CASES[idx]
+    q, k, v, g = prefill_inputs(shape, B, T, hgqa.BF16, (0, 170 + idx, 0))
+    out = run_prefill(shape, hgqa.BF16, q, k, v, g)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), f64(g), spec(shape))
+    assert_close(out, ref, hgqa.BF16, f"waves {waves} case {idx} {shape} B{B} T{T}")
+
+
 def test_peaky_scores():
     """Queries scaled by 8 make the softmax nearly one-hot and the scores 8x
     larger, so the bf16 rounding of the rotated q and k (the MFMA inputs)
