@@ -635,13 +635,16 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 // for 256 rows) when a block visits many tiles: full layers and windows of
 // 1024 keys or more (measured: full layers 4-5% faster, W = 2048 3-4%). 4
 // for short windows, where a workgroup's fixed costs weigh more and two
-// workgroups per CU hide them (W = 512: 8 waves is 9% slower). D = 128
-// without a cache only. HGQA_PREFILL_WAVES=4|8 overrides (tuning only).
+// workgroups per CU hide them (W = 512: 8 waves is 9% slower), and for
+// chunks of fewer than 2048 rows (a few new tokens would leave most of 256
+// rows empty). D = 128 only. HGQA_PREFILL_WAVES=4|8 overrides (tuning only).
 static int prefill_waves(const PrefillArgs& a) {
-  int kw = (a.D == 128 && a.k_cache == nullptr && (!a.sliding || a.window >= 1024)) ? 8 : 4;
+  const bool long_span = !a.sliding || a.window >= 1024;
+  const bool enough_rows = a.k_cache == nullptr || (long long)a.T * a.G >= 2048;
+  int kw = (a.D == 128 && long_span && enough_rows) ? 8 : 4;
   if (const char* env = getenv("HGQA_PREFILL_WAVES")) {
     const int v = atoi(env);
-    if ((v == 4 || v == 8) && a.D == 128 && a.k_cache == nullptr) kw = v;
+    if ((v == 4 || v == 8) && a.D == 128) kw = v;
   }
   return kw;
 }
@@ -661,7 +664,8 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv;
   const dim3 grid((unsigned)blocks), block(kw * 64);
   if (a.D == 128) {
-    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 4>), grid, block, 0, s, a);
+    if (cache && kw == 8) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 8>), grid, block, 0, s, a);
+    else if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 4>), grid, block, 0, s, a);
     else if (kw == 8) hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 8>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 4>), grid, block, 0, s, a);
   } else {

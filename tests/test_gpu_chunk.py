@@ -39,10 +39,7 @@ def _cap(shape, total):
     return shape.window if shape.layer_type == SLIDING else total + 5
 
 
-@pytest.mark.parametrize("idx", range(len(CASES)))
-def test_chunk_matches_whole_sequence_prefill(idx):
-    require_gpu()
-    shape, dtype, p0, n = CASES[idx]
+def _chunk_case(shape, dtype, p0, n, idx):
     total = p0 + n
     what = f"chunk[{idx}] {shape} p0 {p0} n {n}"
     print(what, flush=True)
@@ -70,6 +67,27 @@ def test_chunk_matches_whole_sequence_prefill(idx):
     got = f64(out).reshape(B, n, shape.num_q_heads, shape.head_dim)
     got = np.stack([got[b, t - p0, h] for (b, t, h) in rows])
     assert_close(got, ref, dtype, what)
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)))
+def test_chunk_matches_whole_sequence_prefill(idx):
+    require_gpu()
+    shape, dtype, p0, n = CASES[idx]
+    _chunk_case(shape, dtype, p0, n, idx)
+
+
+# Both workgroup shapes of the bf16 kernel (4 and 8 waves) on chunks over a
+# ring and over a full cache, whatever the launcher would pick.
+WAVE_CASES = [1, 3, 6]
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+@pytest.mark.parametrize("idx", WAVE_CASES)
+def test_chunk_both_workgroup_shapes(idx, waves, monkeypatch):
+    require_gpu()
+    monkeypatch.setenv("HGQA_PREFILL_WAVES", str(waves))
+    shape, dtype, p0, n = CASES[idx]
+    _chunk_case(shape, dtype, p0, n, idx)
 
 
 def test_chunks_in_sequence_equal_one_prefill():
