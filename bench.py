@@ -153,7 +153,7 @@ def bench_step(args, torch, hgqa, synth, workloads, acc):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / acc.PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "attn_prefill (rope pre-pass + prefill_bf16_kernel<128, false>)",
+                     "kernel": "attn_prefill (rope pre-pass + prefill_bf16_kernel<128, false, 4>)",
                      "algorithmic_flops_per_launch": pf_flops},
         "config": {"workload": wl.name, "batch": B, "seq_len": T, "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "window": W, "rope_theta": shape.rope_theta,
