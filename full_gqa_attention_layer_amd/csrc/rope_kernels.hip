@@ -75,7 +75,10 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
 }
 
 // bf16 variant: 16-byte chunks (r is a multiple of 16, so a chunk never
-// straddles r/2 or r and its RoPE partner is a whole chunk too).
+// straddles r/2 or r and its RoPE partner is a whole chunk too). A thread's
+// first kPrefetch chunks (and their partners) are requested before the
+// cos/sin rows are computed, so the loads' latency hides behind the trig.
+constexpr int kPrefetch = 4;
 template <int D>
 __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) {
   constexpr int CH = D / 8;
@@ -84,38 +87,81 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
   const int t0 = blockIdx.x * kPrepassPositions;
   const int np = min(kPrepassPositions, a.T - t0);
   const int half = a.rope.half, rdims = a.rope.rdims;
-  for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
-    int tp = e / half, i = e - tp * half;
-    float2 c = rope_cos_sin(a.p0 + t0 + tp, a.rope.freq_over_pi[i]);
-    cs[tp][i] = c;
-    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
-  }
-  __syncthreads();
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
   uint16_t* kr = static_cast<uint16_t*>(a.k_rot);
   const int Hkv = a.Hkv;
   const int per_pos = Hkv * CH;
-  for (int e = threadIdx.x; e < np * per_pos; e += blockDim.x) {
-    const int tp = e / per_pos;
+  const int total = np * per_pos;
+
+  // chunk e: position t0 + tp, head h, dims d0..d0+7; its source row and the
+  // partner chunk's offset (the chunk itself when it is not rotated)
+  auto locate = [&](int e, int& tp, int& h, int& d0, const uint16_t*& row) {
+    tp = e / per_pos;
     const int r = e - tp * per_pos;
-    const int h = r / CH, d0 = (r - h * CH) * 8;
-    const int t = t0 + tp;
-    const uint16_t* row = k + (((size_t)b * a.T + t) * Hkv + h) * D;
-    u32x4_t raw = *reinterpret_cast<const u32x4_t*>(row + d0);
+    h = r / CH;
+    d0 = (r - h * CH) * 8;
+    row = k + (((size_t)b * a.T + t0 + tp) * Hkv + h) * D;
+  };
+  auto partner = [&](int d0) { return d0 < half ? d0 + half : (d0 < rdims ? d0 - half : d0); };
+  // The frequencies of this thread's (at most two) cos/sin entries come
+  // first: loads retire in issue order, and the trig must not wait for K.
+  static_assert(kPrepassPositions * kMaxHalfRotary <= 2 * 256, "two cos/sin entries per thread");
+  const int ntrig = np * half;
+  const int e0 = threadIdx.x, e1 = threadIdx.x + 256;
+  const double f0 = e0 < ntrig ? a.rope.freq_over_pi[e0 % max(half, 1)] : 0.0;
+  const double f1 = e1 < ntrig ? a.rope.freq_over_pi[e1 % max(half, 1)] : 0.0;
+  u32x4_t raw[kPrefetch], praw[kPrefetch];
+#pragma unroll
+  for (int c = 0; c < kPrefetch; ++c) {
+    // clamped, so the loads form one straight run (a thread past the end
+    // re-reads the last chunk and stores nothing)
+    const int e = min((int)threadIdx.x + 256 * c, total - 1);
+    int tp, h, d0;
+    const uint16_t* row;
+    locate(e, tp, h, d0, row);
+    raw[c] = *reinterpret_cast<const u32x4_t*>(row + d0);
+    praw[c] = *reinterpret_cast<const u32x4_t*>(row + partner(d0));
+  }
+
+  auto trig = [&](int e, double f) {
+    const int tp = e / half, i = e - tp * half;
+    const float2 c = rope_cos_sin(a.p0 + t0 + tp, f);
+    cs[tp][i] = c;
+    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
+  };
+  if (e0 < ntrig) trig(e0, f0);
+  if (e1 < ntrig) trig(e1, f1);
+  __syncthreads();
+
+  auto rotate_store = [&](int e, u32x4_t x, u32x4_t px) {
+    int tp, h, d0;
+    const uint16_t* row;
+    locate(e, tp, h, d0, row);
     if (d0 < rdims) {
       const bool first = d0 < half;
       const int i0 = first ? d0 : d0 - half;
       const float sgn = first ? -1.0f : 1.0f;
-      u32x4_t praw = *reinterpret_cast<const u32x4_t*>(row + (first ? d0 + half : d0 - half));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float2 c0 = cs[tp][i0 + 2 * q], c1 = cs[tp][i0 + 2 * q + 1];
-        const float y0 = fmaf(bf16_lo(raw[q]), c0.x, sgn * bf16_lo(praw[q]) * c0.y);
-        const float y1 = fmaf(bf16_hi(raw[q]), c1.x, sgn * bf16_hi(praw[q]) * c1.y);
-        raw[q] = pack_bf16x2(y0, y1);
+        const float y0 = fmaf(bf16_lo(x[q]), c0.x, sgn * bf16_lo(px[q]) * c0.y);
+        const float y1 = fmaf(bf16_hi(x[q]), c1.x, sgn * bf16_hi(px[q]) * c1.y);
+        x[q] = pack_bf16x2(y0, y1);
       }
     }
-    *reinterpret_cast<u32x4_t*>(kr + (((size_t)b * Hkv + h) * a.T + t) * D + d0) = raw;
+    *reinterpret_cast<u32x4_t*>(kr + (((size_t)b * Hkv + h) * a.T + t0 + tp) * D + d0) = x;
+  };
+#pragma unroll
+  for (int c = 0; c < kPrefetch; ++c) {
+    const int e = threadIdx.x + 256 * c;
+    if (e < total) rotate_store(e, raw[c], praw[c]);
+  }
+  for (int e = threadIdx.x + 256 * kPrefetch; e < total; e += blockDim.x) {
+    int tp, h, d0;
+    const uint16_t* row;
+    locate(e, tp, h, d0, row);
+    rotate_store(e, *reinterpret_cast<const u32x4_t*>(row + d0),
+                 *reinterpret_cast<const u32x4_t*>(row + partner(d0)));
   }
 }
 
