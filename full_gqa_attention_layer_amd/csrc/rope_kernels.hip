@@ -217,9 +217,73 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
   }
 }
 
+// bf16 variant: 16-byte chunks, one per thread. The start position, the
+// RoPE frequency and the thread's first K chunk (with its partner) and V
+// chunk are all requested before anything waits, one round trip for all.
+template <int D>
+__global__ __launch_bounds__(256) void kv_append_bf16_kernel(AppendArgs a) {
+  constexpr int CH = D / 8;
+  __shared__ float2 cs[kMaxHalfRotary];
+  const int n = blockIdx.x + append_first_token(a), b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int half = a.rope.half, rdims = a.rope.rdims;
+  const int Hkv = a.Hkv, nch = Hkv * CH;
+  typedef __attribute__((address_space(1))) const int global_int;
+  int start = a.start_uniform;
+  if (a.start_pos) start = *(global_int*)(a.start_pos + b);
+  const double f = tid < half ? a.rope.freq_over_pi[tid] : 0.0;
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + ((size_t)b * a.n_new + n) * Hkv * D;
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + ((size_t)b * a.n_new + n) * Hkv * D;
+  auto partner = [&](int d0) { return d0 < half ? d0 + half : (d0 < rdims ? d0 - half : d0); };
+  const int e0 = min(tid, nch - 1);  // clamped: one straight run of loads
+  const int h0 = e0 / CH, d00 = (e0 - h0 * CH) * 8;
+  const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(kn + h0 * D + d00);
+  const u32x4_t kp0 = *reinterpret_cast<const u32x4_t*>(kn + h0 * D + partner(d00));
+  const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(vn + h0 * D + d00);
+
+  const int p = start + n;
+  // No early return: the loads above stay ahead of everything that waits
+  // for start_pos; a token that does not reach the cache stores nothing.
+  const bool reaches = p >= 0 && (a.sliding ? p >= start + a.n_new - a.window : p < a.cap);
+  const int slot = a.sliding ? (p >= 0 ? p % a.window : 0) : p;
+  if (tid < half) cs[tid] = rope_cos_sin(p, f);
+  __syncthreads();
+  if (!reaches) return;
+  uint16_t* kc = static_cast<uint16_t*>(a.k_cache);
+  uint16_t* vc = static_cast<uint16_t*>(a.v_cache);
+  auto put = [&](int h, int d0, u32x4_t x, u32x4_t px, u32x4_t v) {
+    if (d0 < rdims) {
+      const bool first = d0 < half;
+      const int i0 = first ? d0 : d0 - half;
+      const float sgn = first ? -1.0f : 1.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float2 c0 = cs[i0 + 2 * q], c1 = cs[i0 + 2 * q + 1];
+        const float y0 = fmaf(bf16_lo(x[q]), c0.x, sgn * bf16_lo(px[q]) * c0.y);
+        const float y1 = fmaf(bf16_hi(x[q]), c1.x, sgn * bf16_hi(px[q]) * c1.y);
+        x[q] = pack_bf16x2(y0, y1);
+      }
+    }
+    const size_t dst = (((size_t)b * Hkv + h) * a.cap + slot) * D + d0;
+    *reinterpret_cast<u32x4_t*>(kc + dst) = x;
+    *reinterpret_cast<u32x4_t*>(vc + dst) = v;
+  };
+  if (tid < nch) put(h0, d00, k0, kp0, v0);
+  for (int e = tid + 256; e < nch; e += 256) {
+    const int h = e / CH, d0 = (e - h * CH) * 8;
+    put(h, d0, *reinterpret_cast<const u32x4_t*>(kn + h * D + d0),
+        *reinterpret_cast<const u32x4_t*>(kn + h * D + partner(d0)),
+        *reinterpret_cast<const u32x4_t*>(vn + h * D + d0));
+  }
+}
+
 hipError_t launch_kv_append(const AppendArgs& a, Elem e, hipStream_t s) {
   dim3 grid(a.n_new - append_first_token(a), a.B);
-  if (e == Elem::BF16)
+  if (e == Elem::BF16 && a.D == 128)
+    hipLaunchKernelGGL(kv_append_bf16_kernel<128>, grid, dim3(256), 0, s, a);
+  else if (e == Elem::BF16 && a.D == 64)
+    hipLaunchKernelGGL(kv_append_bf16_kernel<64>, grid, dim3(256), 0, s, a);
+  else if (e == Elem::BF16)
     hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(kv_append_kernel<float>, grid, dim3(256), 0, s, a);
