@@ -239,27 +239,43 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     koff[i] = 2u * (uint32_t)(key * D + 8 * (pos ^ Swz<D>::k(key)));
   }
   const int key_l = wave * PER_WAVE * KPP + lane / CH;  // the lane's key in the wave's first piece
-  const uint32_t voff = 2u * (__umul24(key_l, (unsigned)vstride) + 8 * ((lane % CH) ^ Swz<D>::v(key_l)));
+  const uint32_t vswz = 8 * ((lane % CH) ^ Swz<D>::v(key_l));
+  const uint32_t voff = 2u * (__umul24(key_l, (unsigned)vstride) + vswz);
+  // V in a cache has rows D apart (a chunk's V rows are Hkv D apart).
+  const uint32_t vcoff = 2u * ((uint32_t)key_l * D + vswz);
   auto load_tile = [&](int j0, int st) {
     const int kmax = j_last - j0;
-    const char* kt = reinterpret_cast<const char*>(kbase + (size_t)(j0 - p0) * D);
-    const char* vt = reinterpret_cast<const char*>(vbase + (size_t)(j0 - p0) * vstride);
-    auto issue = [&](int I, const void* ksrc, const void* vsrc) {
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
-    };
-    if (!kCache && kmax >= kBN - 1) {
-      const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kt, kBN * D * 2);
-      const __amdgpu_buffer_rsrc_t vres = tile_rsrc(vt, (uint32_t)(((kBN - 1) * vstride + D) * 2));
+    // a whole tile through buffer descriptors: uniform bases, the lane
+    // offsets above, no vector arithmetic
+    auto whole = [&](const void* kb, const void* vb, uint32_t vo, uint32_t vrow, uint32_t vbytes) {
+      const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kb, kBN * D * 2);
+      const __amdgpu_buffer_rsrc_t vres = tile_rsrc(vb, vbytes);
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int I = wave * PER_WAVE + i;
         copy16_to_lds(kres, (lds_void_t*)&sm.st[st].k[512 * I], koff[i], 0u);
-        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], voff,
-                      (uint32_t)(i * KPP * vstride * 2));
+        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], vo, (uint32_t)i * KPP * vrow * 2);
       }
+    };
+    if (kmax >= kBN - 1 && j0 >= p0) {  // every key in this call's chunk
+      whole(kbase + (size_t)(j0 - p0) * D, vbase + (size_t)(j0 - p0) * vstride, voff,
+            (uint32_t)vstride, (uint32_t)(((kBN - 1) * vstride + D) * 2));
       return;
     }
+    if constexpr (kCache) {
+      // every key in the cache, in consecutive slots
+      const int slot0 = a.ring ? j0 % a.cap : j0;
+      if (j0 + kBN <= p0 && slot0 + kBN <= a.cap) {
+        const size_t off = cache_head + (size_t)slot0 * D;
+        whole(static_cast<const uint16_t*>(a.k_cache) + off,
+              static_cast<const uint16_t*>(a.v_cache) + off, vcoff, D, kBN * D * 2);
+        return;
+      }
+    }
+    auto issue = [&](int I, const void* ksrc, const void* vsrc) {
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
+    };
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int I = wave * PER_WAVE + i;
