@@ -225,11 +225,12 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   // both tiles. Keys past the end re-read the last key: finite values that
   // the causal mask hides (their probabilities are exactly 0). In a chunk,
   // keys before p0 come from the cache: slot j, or j mod cap in a ring.
-  // Byte offsets of this wave's pieces inside a tile. A tile that ends at or
-  // before the last key is then a uniform base plus these fixed lane offsets,
-  // with no per-tile address arithmetic.
-  // V's swizzle repeats every KPP keys (the keys of one piece), so its
-  // pieces sit a fixed stride apart and one lane offset serves them all.
+  //
+  // koff / voff are the byte offsets of this lane's pieces inside a tile, so
+  // a whole tile (ending at or before the last key, wholly in the chunk or
+  // wholly in consecutive cache slots) is a uniform base plus fixed lane
+  // offsets. V's swizzle repeats every KPP keys (the keys of one piece), so
+  // its pieces sit a fixed stride apart and one lane offset serves them all.
   constexpr int KPP = 64 / CH;  // keys per 1 KB piece
   uint32_t koff[PER_WAVE];
 #pragma unroll
@@ -294,9 +295,10 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     }
   };
 
-  // ---- the block's Q rows go to stage 1 (idle until the loop starts), four
-  // whole rows per 1 KB piece; chunk c of row r sits at position c ^ swz(r),
-  // the layout K tiles use, so the fragment reads below are conflict-free.
+  // ---- the block's Q rows go to stage 1 (idle until the loop starts) or,
+  // with 8 waves, to the Q/output area; four whole rows per 1 KB piece. Chunk
+  // c of row r sits at position c ^ swz(r), the layout K tiles use, so the
+  // fragment reads below are conflict-free.
   {
     constexpr int Q_PIECES = kRows * D * 2 / 1024 / kWaves;
     uint16_t* qs = KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[1]);
@@ -543,8 +545,9 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   else tile(ntiles - 1, Full{}, Later{});
 
   // ---- epilogue: normalise and gate in registers, then turn the O^T
-  // fragments into row-major rows in LDS (stage 0 is idle: the loop ended on
-  // a barrier with no load in flight) so that the stores write whole rows.
+  // fragments into row-major rows in LDS (stage 0, idle because the loop
+  // ended on a barrier with no load in flight, or with 8 waves the Q/output
+  // area) so that the stores write whole rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = row_ok ? sigmoidf_dev(gate_logit) / l_tot : 0.0f;
   uint16_t* ow = (KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[0])) + wave * (kRowsPerWave * D);  // this wave's rows
