@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -51,10 +52,15 @@ def parse():
 
 
 def source_hash(names):
+    """Hash of the kernel sources' code: comments and layout are dropped, so
+    a comment edit keeps a counter summary valid and any code edit does not."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "full_gqa_attention_layer_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "full_gqa_attention_layer_amd", "csrc", n)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
