@@ -11,7 +11,8 @@
 //   O^T (D x 16 heads)      += V^T (D x 32 keys) * P^T
 // The G query heads of the KV group sit in the 16 MFMA columns, so each K/V
 // byte is read from HBM once for all G heads. K is loaded straight into the
-// A-operand layout; V is transposed through a per-wave LDS tile. Waves merge
+// A-operand layout; V is transposed through a per-wave LDS tile. Each wave
+// keeps two chunks in flight (two K register sets, two V tiles). Waves merge
 // their (max, sum, output) in LDS; with one split the workgroup writes the
 // gated output, otherwise it writes a partial that the merge kernel combines
 // by log-sum-exp.
@@ -55,25 +56,59 @@ template <> struct DecSwz<64> {
   static __device__ __forceinline__ int v(int key) { return 2 * ((key >> 1) & 3); }
 };
 
+// Max and sum over the four 16-lane rows of a wave (the g index of the
+// 16x16 MFMA layout) with the row-swap permutes: one swap exchanges rows
+// 0<->1 and 2<->3, the other the two 32-lane halves.
+__device__ __forceinline__ float rows_max(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const uint32_t c = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const uint32_t c = __float_as_uint(x);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
+// The V buffer that chunks 0, 2, 4, ... of each wave go through; the wave
+// merge at the end reuses it. Chunks 1, 3, 5, ... go through a second LDS
+// object, and each wave's cos/sin row sits in a third: the compiler tracks
+// HBM -> LDS copies per object, so reading one buffer does not wait for
+// copies still in flight into the other.
 template <int D>
 struct DecodeLds {
   union {
-    uint16_t v[kDecWaves][2][kChunk * D];  // per-wave double-buffered V chunks
+    uint16_t v[kDecWaves][kChunk * D];
     struct {
-      float o[kDecWaves][16][D];
-      float m[kDecWaves][16];
-      float l[kDecWaves][16];
+      float o[kDecWaves][16][D];  // per wave and head, swizzled 16-byte columns
+      float m[16][kDecWaves];
+      float l[16][kDecWaves];
+      float gate[16];  // sigmoid of each head's gate
     } mg;
   } u;
-  float2 cs[kMaxHalfRotary];
 };
+
+// A buffer descriptor over `bytes` from `base`: loads at offsets past it
+// return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dec_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) {
   constexpr int NS = D / 32;          // k-steps of 32 dims
   constexpr int NDB = D / 16;         // 16-dim blocks of the output
   constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int ROW = 2 * D;          // bytes per cached key
   __shared__ DecodeLds<D> sm;
+  __shared__ uint16_t vbuf_odd[kDecWaves][kChunk * D];
+  __shared__ float2 cs_rows[kDecWaves][kMaxHalfRotary];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,10 +127,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   const int n_vis = a.sliding ? min(L, a.window) : L;
   const int k_begin = split * a.split_keys;
   if (k_begin >= n_vis) return;
-  const int k_end = min(n_vis, k_begin + a.split_keys);
+  const int nrel = min(n_vis, k_begin + a.split_keys) - k_begin;  // keys of this split
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + (size_t)(b * Hkv + kvh) * a.cap * D;
+  const size_t head0 = (size_t)(b * Hkv + kvh) * a.cap + k_begin;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_cache) + head0 * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_cache) + head0 * D;
 
   f32x4_t O[NDB];
 #pragma unroll
@@ -103,47 +139,58 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   float m_run = -INFINITY, l_run = 0.0f;
   const float sc = a.scale * kLog2eDec;
 
-  // Chunk loads: K straight into the MFMA A-operand layout (lane holds key
-  // n16 + 16 kb, dims 32s+8g..+7), V from HBM into the wave's LDS buffer.
-  // Keys past the split re-read its last key; their scores are masked.
-  constexpr int VDMA = kChunk * CH / 64;  // 1 KB HBM->LDS pieces per V chunk
-  auto issue = [&](int key0, u32x4_t (&kf)[2][NS], uint16_t* vbuf) {
+  // Chunk loads through descriptors that end at the split's last key, so a
+  // chunk's keys past it read as zeros and every chunk issues the same
+  // instructions (no branch around a load: the compiler then waits for
+  // exactly the chunk it needs). K goes straight into the MFMA A-operand
+  // layout (lane: key n16 + 16 kb, dims 32s + 8g..+7), V from HBM into the
+  // wave's LDS buffer in 1 KB pieces.
+  constexpr int VDMA = kChunk * CH / 64;
+  constexpr int RPP = 64 / CH;                       // key rows per V piece
+  const uint32_t koff0 = (uint32_t)(n16 * ROW + 16 * g);
+  const uint32_t koff1 = koff0 + 16 * ROW;
+  uint32_t voff[2];  // lane offset of V pieces i even / odd (the swizzle differs)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(key0 + 16 * kb + n16, k_end - 1);
+  for (int p = 0; p < 2; ++p) {
+    const int row = RPP * p + lane / CH, pos = lane % CH;
+    voff[p] = (uint32_t)((lane / CH) * ROW + 16 * (pos ^ DecSwz<D>::v(row)));
+  }
+  auto issue = [&](int rel, u32x4_t (&kf)[2][NS], uint16_t* vbuf) {
+    // (uniform; readfirstlane keeps the descriptor in scalar registers)
+    const int left = __builtin_amdgcn_readfirstlane(min(max(nrel - rel, 0), kChunk) * ROW);
+    const __amdgpu_buffer_rsrc_t kr = dec_rsrc(kbase + (size_t)rel * D, left);
+    const __amdgpu_buffer_rsrc_t vr = dec_rsrc(vbase + (size_t)rel * D, left);
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        kf[kb][s] = *reinterpret_cast<const u32x4_t*>(kbase + (size_t)key * D + 32 * s + 8 * g);
+    for (int s = 0; s < NS; ++s) {
+      kf[0][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, koff0 + 64 * s, 0, 0));
+      kf[1][s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(kr, koff1 + 64 * s, 0, 0));
     }
 #pragma unroll
-    for (int i = 0; i < VDMA; ++i) {
-      const int P = 64 * i + lane;
-      const int row = P / CH, pos = P % CH;
-      const int key = min(key0 + row, k_end - 1);
-      const uint16_t* src = vbase + (size_t)key * D + 8 * (pos ^ DecSwz<D>::v(row));
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(vbuf + 512 * i), 16, 0, 0);
-    }
+    for (int i = 0; i < VDMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vbuf + 512 * i), 16,
+                                               voff[i & 1] + (uint32_t)(i * RPP * ROW), 0, 0, 0);
   };
 
-  // The first chunk starts moving, then q (with each chunk's RoPE partner)
-  // and the RoPE frequencies are requested right behind it, so one memory
-  // round trip brings all three. (The compiler waits for every outstanding
-  // load before a register loaded next to an HBM -> LDS copy is used.)
+  // The wave's first two chunks start moving, with q (and each q chunk's
+  // RoPE partner), the gate and the RoPE frequency between them, so one
+  // memory round trip brings the first chunk, q, gate and frequency, and the
+  // second chunk is already in flight when the key loop starts.
   constexpr int STEP = kChunk * kDecWaves;
   u32x4_t kfa[2][NS], kfb[2][NS];
-  uint16_t* va_buf = sm.u.v[wave][0];
-  uint16_t* vb_buf = sm.u.v[wave][1];
-  int key0 = k_begin + kChunk * wave;
-  if (key0 < k_end) issue(key0, kfa, va_buf);
+  uint16_t* va_buf = sm.u.v[wave];
+  uint16_t* vb_buf = vbuf_odd[wave];
+  const int rel0 = kChunk * wave;
+  issue(rel0, kfa, va_buf);
 
   const int half = a.rope.half, rdims = a.rope.rdims;
-  static_assert(kMaxHalfRotary <= kDecThreads, "one frequency per thread");
-  const double freq = tid < half ? a.rope.freq_over_pi[tid] : 0.0;
+  static_assert(kMaxHalfRotary == 64, "one frequency per lane");
+  const double freq = a.rope.freq_over_pi[lane];
   const bool hv = n16 < G;
+  const size_t qh = (size_t)b * a.Hq + kvh * G + (hv ? n16 : 0);
+  const float gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[qh]);
   u32x4_t qraw[NS], qpart[NS];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((size_t)b * a.Hq + kvh * G + (hv ? n16 : 0)) * D;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + qh * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int d0 = 32 * s + 8 * g;
@@ -152,10 +199,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
       qpart[s] = *reinterpret_cast<const u32x4_t*>(qrow + dp);
     }
   }
+  issue(rel0 + STEP, kfb, vb_buf);
 
-  // ---- rotate q at position L-1; lane holds head n16, dims 32s+8g..+7
-  if (tid < half) sm.cs[tid] = rope_cos_sin(L - 1, freq);
-  __syncthreads();
+  // ---- rotate q at position L-1; lane holds head n16, dims 32s+8g..+7.
+  // Every wave forms its own cos/sin row (lane i: frequency i), so no
+  // workgroup barrier stands between the first loads and the key loop, and
+  // the frequency load has no branch around it.
+  float2* cs = cs_rows[wave];
+  cs[lane] = rope_cos_sin(L - 1, freq);
   bf16x8_t qf[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -166,16 +217,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
       x[2 * e] = bf16_lo(qraw[s][e]);
       x[2 * e + 1] = bf16_hi(qraw[s][e]);
     }
-    if (d0 < rdims) {
-      const bool first = d0 < half;
-      const int i0 = first ? d0 : d0 - half;
-      const float sgn = first ? -1.0f : 1.0f;
+    // Rotated dims take the rotation, the rest pass through; a select, not a
+    // branch, so the partner load is not moved into a branch behind the
+    // chunks in flight.
+    const bool rot = d0 < rdims, first = d0 < half;
+    const int i0 = first ? d0 : (rot ? d0 - half : 0);
+    const float sgn = first ? -1.0f : 1.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float2 c0 = sm.cs[i0 + 2 * e], c1 = sm.cs[i0 + 2 * e + 1];
-        x[2 * e] = fmaf(x[2 * e], c0.x, sgn * bf16_lo(qpart[s][e]) * c0.y);
-        x[2 * e + 1] = fmaf(x[2 * e + 1], c1.x, sgn * bf16_hi(qpart[s][e]) * c1.y);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float2 c0 = cs[i0 + 2 * e], c1 = cs[i0 + 2 * e + 1];
+      const float y0 = fmaf(x[2 * e], c0.x, sgn * bf16_lo(qpart[s][e]) * c0.y);
+      const float y1 = fmaf(x[2 * e + 1], c1.x, sgn * bf16_hi(qpart[s][e]) * c1.y);
+      x[2 * e] = rot ? y0 : x[2 * e];
+      x[2 * e + 1] = rot ? y1 : x[2 * e + 1];
     }
     u32x4_t packed;
 #pragma unroll
@@ -189,7 +243,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
   const int vrow0 = 4 * g + (r16 >> 2);
   const int vdim = 4 * (r16 & 3);
 
-  auto compute = [&](int key0, const u32x4_t (&kf)[2][NS], const uint16_t* vbuf) {
+  // One chunk: scores, online softmax, PV. A chunk whose keys all lie past
+  // the split (only ever the second of a pair, after a chunk with keys)
+  // leaves the state unchanged: its scores are -inf and its V rows zeros.
+  auto compute = [&](int rel, const u32x4_t (&kf)[2][NS], const uint16_t* vbuf) {
     f32x4_t S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -199,19 +256,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
         S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[kb][s]),
                                                          qf[s], S[kb], 0, 0, 0);
     }
-    // mask keys past the split; online softmax per head (column n16)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int key = key0 + 16 * kb + 4 * g + v;
-        if (key >= k_end) S[kb][v] = -INFINITY;
+        if (rel + 16 * kb + 4 * g + v >= nrel) S[kb][v] = -INFINITY;
         mx = fmaxf(mx, S[kb][v]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * sc);
+    const float m_new = fmaxf(m_run, rows_max(mx) * sc);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.0f;
@@ -247,69 +300,76 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     }
   };
 
-  // Double-buffered chunk loop: the next chunk's loads are in flight while
-  // the current one is computed. Unrolled by two so buffers are static.
-  while (key0 < k_end) {
-    const int k1 = key0 + STEP;
-    if (k1 < k_end) {
-      issue(k1, kfb, vb_buf);
-      vm_wait_keep<2 * NS + VDMA>();
-    } else {
-      vm_wait_keep<0>();
-    }
-    compute(key0, kfa, va_buf);
-    if (k1 >= k_end) break;
-    const int k2 = k1 + STEP;
-    __builtin_amdgcn_wave_barrier();  // buffer a is consumed before it is refilled
-    if (k2 < k_end) {
-      issue(k2, kfa, va_buf);
-      vm_wait_keep<2 * NS + VDMA>();
-    } else {
-      vm_wait_keep<0>();
-    }
-    compute(k1, kfb, vb_buf);
-    __builtin_amdgcn_wave_barrier();
-    key0 = k2;
+  // Chunks in pairs, two in flight: while chunk c is computed, chunk c + 1
+  // is arriving; chunk c + 2 is requested into c's buffers once c is done.
+  // Every wave issues the same loads each pair, so the waits stay exact.
+  const int nch = rel0 < nrel ? (nrel - rel0 + STEP - 1) / STEP : 0;
+  for (int pr = 0; pr < (nch + 1) / 2; ++pr) {
+    const int r = rel0 + 2 * pr * STEP;
+    // Scheduling fences around each refill: the buffer's reads (consumed by
+    // the products above) are done before its copies are issued, and the
+    // next chunk's products stay below, so no wait for that chunk holds the
+    // refill up.
+    vm_wait_keep<2 * NS + VDMA>();
+    compute(r, kfa, va_buf);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(r + 2 * STEP, kfa, va_buf);
+    __builtin_amdgcn_sched_barrier(0);
+    vm_wait_keep<2 * NS + VDMA>();
+    compute(r + STEP, kfb, vb_buf);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(r + 3 * STEP, kfb, vb_buf);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- merge the waves of this workgroup
-  float l_w = l_run + __shfl_xor(l_run, 16, 64);
-  l_w += __shfl_xor(l_w, 32, 64);
-  __syncthreads();  // every wave is done with its V^T tile (aliased below)
+  const float l_w = rows_sum(l_run);
+  __builtin_amdgcn_s_waitcnt(0);  // the trailing copies into buffer a have landed
+  __syncthreads();                // every wave is done with its buffer a (aliased below)
   if (g == 0) {
-    sm.u.mg.m[wave][n16] = m_run;
-    sm.u.mg.l[wave][n16] = l_w;
+    sm.u.mg.m[n16][wave] = m_run;
+    sm.u.mg.l[n16][wave] = l_w;
+    if (wave == 0) sm.u.mg.gate[n16] = sigmoidf_dev(gv);
   }
+  // Lane (n16, g) holds dims 16db + 4g..+3 of head n16. Each head's row is
+  // kept as 16-byte columns XOR-swizzled by the head, so the 16 heads of a
+  // write land in distinct banks and a read of consecutive columns of one
+  // head stays conflict-free.
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sm.u.mg.o[wave][n16][16 * db + 4 * g + v] = O[db][v];
+    *reinterpret_cast<f32x4_t*>(&sm.u.mg.o[wave][n16][4 * ((4 * db + g) ^ n16)]) = O[db];
   __syncthreads();
 
-  for (int idx = tid; idx < G * D; idx += kDecThreads) {
-    const int hh = idx / D, d = idx - hh * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, sm.u.mg.m[w][hh]);
-    float acc = 0.0f, lsum = 0.0f;
+  // One thread per (head, 4 dims): weights of the waves from their maxima,
+  // the weighted sum of their outputs, then the gate (one split) or a
+  // partial for the merge kernel.
+  static_assert(kDecWaves == 4, "one float4 of maxima / sums per head");
+  constexpr int C4 = D / 4;
+  for (int it = tid; it < G * C4; it += kDecThreads) {
+    const int hh = it / C4, c4 = it % C4;
+    const f32x4_t mw = *reinterpret_cast<const f32x4_t*>(sm.u.mg.m[hh]);
+    const f32x4_t lw = *reinterpret_cast<const f32x4_t*>(sm.u.mg.l[hh]);
+    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    f32x4_t acc = {};
+    float lsum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kDecWaves; ++w) {
-      const float f = __builtin_amdgcn_exp2f(sm.u.mg.m[w][hh] - M);
-      acc = fmaf(sm.u.mg.o[w][hh][d], f, acc);
-      lsum = fmaf(sm.u.mg.l[w][hh], f, lsum);
+      const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+      acc += f * *reinterpret_cast<const f32x4_t*>(&sm.u.mg.o[w][hh][4 * (c4 ^ hh)]);
+      lsum = fmaf(lw[w], f, lsum);
     }
-    const int h = kvh * G + hh;
+    const size_t row = (size_t)b * a.Hq + kvh * G + hh;
     if (a.num_splits == 1) {
-      const float gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[(size_t)b * a.Hq + h]);
-      static_cast<uint16_t*>(a.out)[((size_t)b * a.Hq + h) * D + d] =
-          f32_to_bf16(sigmoidf_dev(gv) * acc / lsum);
+      const float gs = sm.u.mg.gate[hh];
+      u32x2_t packed;
+      packed[0] = pack_bf16x2(gs * acc[0] / lsum, gs * acc[1] / lsum);
+      packed[1] = pack_bf16x2(gs * acc[2] / lsum, gs * acc[3] / lsum);
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + row * D + 4 * c4) = packed;
     } else {
-      float* part = a.partial + (((size_t)b * a.Hq + h) * a.num_splits + split) * (D + 2);
-      part[d] = acc;
-      if (d == 0) {
-        part[D] = M;
-        part[D + 1] = lsum;
-      }
+      float* part = a.partial + (row * a.num_splits + split) * (D + 2);
+      *reinterpret_cast<float2*>(part + 4 * c4) = make_float2(acc[0], acc[1]);
+      *reinterpret_cast<float2*>(part + 4 * c4 + 2) = make_float2(acc[2], acc[3]);
+      if (c4 == 0) *reinterpret_cast<float2*>(part + D) = make_float2(M, lsum);
     }
   }
 }

@@ -193,7 +193,6 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   int dt_row, hg_row;
   split_local(min(rl, nrows - 1), dt_row, hg_row);
   const int t_row = t0 + dt_row;
-  const int h = kvh * G + hg_row;
 
   const int t_lo = t0;
   const int t_hi = t0 + pos_of_local(nrows - 1);
