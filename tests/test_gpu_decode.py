@@ -229,6 +229,43 @@ def test_decode_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("split_keys", [None, 128, 1024, 1 << 20])
+def test_split_counts_agree(split_keys, monkeypatch):
+    """The same decode with the keys cut into different split counts (the
+    tuning override fixes the keys per split; 1 << 20 gives one split). Every
+    plan matches the oracle. Against the one-split output the difference is
+    bounded by the one rounding that depends on the plan: each probability is
+    rounded to bf16 (relative error <= 2^-9) relative to its own split's
+    running maximum, so two plans differ by at most 2 * 2^-9 * sigmoid(gate) *
+    max |v| over the sequence's keys, plus one bf16 step of the output."""
+    require_gpu()
+    shape = LayerShape(FULL, 0, 16, 2, 128, 5e6, 0.5)
+    lens = [1, 100, 4000, 20000]
+    kc, vc, okc, ovc, _ = build_caches(shape, hgqa.BF16, lens, (0, 303, 0))
+    q = synth.host_normal((4, 16, 128), (0, 303, 0, synth.Q)).to(DEV)
+    g = synth.host_normal((4, 16), (0, 303, 0, synth.GATE)).to(DEV)
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    monkeypatch.setenv("HGQA_DECODE_SPLIT_KEYS", str(1 << 20))
+    one = hgqa.attn_decode(L, q, g, kc, vc, seq, max(lens))
+    if split_keys is None:
+        monkeypatch.delenv("HGQA_DECODE_SPLIT_KEYS")
+    else:
+        monkeypatch.setenv("HGQA_DECODE_SPLIT_KEYS", str(split_keys))
+    out = hgqa.attn_decode(L, q, g, kc, vc, seq, max(lens))
+    torch.cuda.synchronize()
+    ref = oracle.decode(f64(q), f64(g), okc, ovc, lens, spec(shape))
+    assert_close(out, ref, hgqa.BF16, f"split_keys {split_keys}")
+    a, b = f64(out), f64(one)
+    G = shape.num_q_heads // shape.num_kv_heads
+    sig = 1.0 / (1.0 + np.exp(-f64(g)))                                   # [B, Hq]
+    vmax = np.stack([np.abs(ovc[i, :, :n]).max(axis=(1, 2)) for i, n in enumerate(lens)])
+    bound = 2.0 ** -8 * sig * np.repeat(vmax, G, axis=1)                  # [B, Hq]
+    tol = bound[:, :, None] + 2.0 ** -7 * np.abs(b) + 1e-6
+    assert np.all(np.abs(a - b) <= tol), \
+        f"split_keys {split_keys}: max diff {np.abs(a - b).max():.3e} from the one-split output"
+
+
 # ------------------------------------------------------------ full size
 
 def _c5_state(layer_index):
