@@ -162,3 +162,19 @@ def test_decode_argument_checks(lib):
     Lg.gqa_ratio = 32
     assert lib.attn_decode(ctypes.byref(Lg), 1, p, p, p, p, 100, p, 10, p, 1 << 20, p,
                            None) == hgqa.EUNSUPPORTED
+
+
+def test_decode_split_plan(lib):
+    """The host split plan, seen through the workspace it asks for
+    (B * Hq * splits * (D + 2) fp32, none for one split): the batched full
+    layer takes 4 splits of 32768 keys, a 512-slot ring of 64 sequences one
+    split, and a lone short batch many splits of 128 keys."""
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    per_split = 64 * (128 + 2) * 4                      # one sequence, all heads
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072, 131072) == \
+        64 * 4 * per_split
+    Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Ls), 64, 131072, 512) == 0
+    # 8 (sequence, KV head) pairs: aim for 2048 workgroups, at least 128 keys each
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000, 20000) == \
+        1 * 157 * per_split
