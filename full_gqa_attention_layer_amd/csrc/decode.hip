@@ -16,8 +16,6 @@
 // their (max, sum, output) in LDS; with one split the workgroup writes the
 // gated output, otherwise it writes a partial that the merge kernel combines
 // by log-sum-exp.
-#include <cstdlib>
-
 #include "device_util.h"
 
 namespace hgqa {
@@ -469,7 +467,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 }
 
 DecodePlan plan_decode(Elem e, int B, int Hq, int Hkv, int D, int sliding, int window,
-                       int max_seq_len) {
+                       int max_seq_len, int split_keys_override) {
   DecodePlan p{};
   const int n_vis_max = sliding ? (max_seq_len < window ? max_seq_len : window) : max_seq_len;
   if (e == Elem::F32 || n_vis_max <= 0) {
@@ -479,18 +477,13 @@ DecodePlan plan_decode(Elem e, int B, int Hq, int Hkv, int D, int sliding, int w
     return p;
   }
   const long long pairs = (long long)B * Hkv;
-  // HGQA_DECODE_SPLIT_KEYS (tuning only) fixes the keys per split.
-  if (const char* env = getenv("HGQA_DECODE_SPLIT_KEYS")) {
-    long long sk = atoll(env);
-    if (sk > 0) {
-      sk = (sk + kChunk - 1) / kChunk * kChunk;
-      p.split_keys = (int)(sk < n_vis_max ? sk : (n_vis_max + kChunk - 1) / kChunk * kChunk);
-      p.num_splits = (n_vis_max + p.split_keys - 1) / p.split_keys;
-      p.workspace_bytes = p.num_splits > 1
-                              ? (size_t)B * Hq * p.num_splits * (size_t)(D + 2) * sizeof(float)
-                              : 0;
-      return p;
-    }
+  if (split_keys_override > 0) {
+    long long sk = (split_keys_override + kChunk - 1) / kChunk * kChunk;
+    p.split_keys = (int)(sk < n_vis_max ? sk : (n_vis_max + kChunk - 1) / kChunk * kChunk);
+    p.num_splits = (n_vis_max + p.split_keys - 1) / p.split_keys;
+    p.workspace_bytes =
+        p.num_splits > 1 ? (size_t)B * Hq * p.num_splits * (size_t)(D + 2) * sizeof(float) : 0;
+    return p;
   }
   // Enough workgroups to fill the chip and balance unequal lengths, but no
   // split below kDecMinKeysPerBlock keys when there are many (sequence, KV

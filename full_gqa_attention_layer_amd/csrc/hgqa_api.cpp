@@ -2,6 +2,7 @@
 // dispatch to the gfx950 kernels. Nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -14,6 +15,10 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// hgqa_set_tuning overrides (0: the library's own choice).
+std::atomic<int> g_prefill_waves{0};
+std::atomic<int> g_decode_split_keys{0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -121,14 +126,24 @@ void fill_rope(const Layer& l, hgqa::RopeArgs* r) {
 // and block counts within the grid limit.
 constexpr long long kMaxElems = 1LL << 40;
 
+// Rotated K [B,Hkv,T,D], then the cos/sin table: [T, r/2] shared by every
+// sequence of a prompt at positions 0.., or [B, T, r/2] for chunks whose
+// sequences start at their own positions.
+size_t rotated_k_bytes(const Layer& l, int B, int T) {
+  return round256((size_t)B * l.Hkv * T * l.D * l.esize);
+}
 size_t prefill_ws(const Layer& l, int B, int T) {
-  return round256((size_t)B * l.Hkv * T * l.D * l.esize) + round256((size_t)T * l.half * sizeof(float2));
+  return rotated_k_bytes(l, B, T) + round256((size_t)T * l.half * sizeof(float2));
+}
+size_t chunk_ws(const Layer& l, int B, int T) {
+  return rotated_k_bytes(l, B, T) + round256((size_t)B * T * l.half * sizeof(float2));
 }
 
-// Checks shared by the prefill entry points; n = tokens in this call.
+// Checks shared by the prefill entry points; n = tokens in this call, need =
+// the workspace bytes the call needs.
 int check_prefill_call(const Layer& l, int batch, int n, const void* q, const void* k,
                        const void* v, const void* gate, const void* out, const void* workspace,
-                       size_t workspace_bytes) {
+                       size_t workspace_bytes, size_t need) {
   if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
   if ((long long)batch * n * l.Hq * l.D > kMaxElems)
     return fail(HGQA_EUNSUPPORTED, "problem too large");
@@ -139,7 +154,6 @@ int check_prefill_call(const Layer& l, int batch, int n, const void* q, const vo
     return fail(HGQA_EINVAL, "a tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
     return fail(HGQA_EINVAL, "q, k, v, out and workspace must be 16-byte aligned");
-  const size_t need = prefill_ws(l, batch, n);
   if (workspace_bytes < need)
     return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
   if (out == q || out == k || out == v || out == gate)
@@ -156,8 +170,11 @@ hgqa::PrefillArgs prefill_args(const Layer& l, int batch, int n, const void* q, 
   a.gate = gate;
   a.out = out;
   a.k_rot = workspace;
-  a.cs_table = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
-                                         round256((size_t)batch * l.Hkv * n * l.D * l.esize));
+  a.cs_table = reinterpret_cast<float2*>(static_cast<char*>(workspace) + rotated_k_bytes(l, batch, n));
+  a.cs_bstride = 0;
+  a.start_pos = nullptr;
+  a.max_end_pos = n;
+  a.waves = g_prefill_waves.load(std::memory_order_relaxed);
   a.B = batch;
   a.T = n;
   a.Hq = l.Hq;
@@ -172,6 +189,84 @@ hgqa::PrefillArgs prefill_args(const Layer& l, int batch, int n, const void* q, 
 }
 
 }  // namespace
+
+int hgqa::decode_call(const void* layer_ptr, int batch, const void* q, const void* gate,
+                      const void* k_cache, const void* v_cache, int cache_capacity,
+                      const int32_t* seq_lens, int max_seq_len, void* workspace,
+                      size_t workspace_bytes, void* out, void* stream, ScratchFn scratch_fn,
+                      size_t scratch_bytes) {
+  const hgqa_layer* layer = static_cast<const hgqa_layer*>(layer_ptr);
+  Layer l;
+  int rc = check_layer(layer, &l);
+  if (rc != HGQA_OK) return rc;
+  if (batch < 0) return fail(HGQA_EINVAL, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
+  if (max_seq_len < 1) return fail(HGQA_EINVAL, "max_seq_len must be >= 1");
+  if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
+  if (l.sliding && cache_capacity != l.window)
+    return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
+                l.window, cache_capacity);
+  if (!l.sliding && max_seq_len > cache_capacity)
+    return fail(HGQA_ENOSPACE, "max_seq_len %d exceeds the full cache capacity %d", max_seq_len,
+                cache_capacity);
+  if (l.elem == hgqa::Elem::BF16 && l.G > 16)
+    return fail(HGQA_EUNSUPPORTED, "bf16 decode supports gqa_ratio <= 16 (got %d)", l.G);
+  if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
+    return fail(HGQA_EUNSUPPORTED, "cache too large");
+  if (!q || !gate || !k_cache || !v_cache || !seq_lens || !out)
+    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(HGQA_EINVAL, "q, the caches and out must be 16-byte aligned");
+  if (out == q || out == gate) return fail(HGQA_EINVAL, "out must not alias an input");
+  const hgqa::DecodePlan plan =
+      hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len,
+                        g_decode_split_keys.load(std::memory_order_relaxed));
+  if (scratch_fn && plan.workspace_bytes > 0) {
+    if (plan.workspace_bytes > scratch_bytes)
+      return fail(HGQA_ENOSPACE,
+                  "this decode needs %zu bytes of split partials; the library's static scratch "
+                  "holds %zu (use attn_decode with a workspace)",
+                  plan.workspace_bytes, scratch_bytes);
+    hipError_t e = scratch_fn(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess)
+      return fail(HGQA_EHIP, "decode scratch set-up failed: %s", hipGetErrorString(e));
+    workspace_bytes = scratch_bytes;
+  }
+  if (plan.workspace_bytes > 0) {
+    if (!workspace) return fail(HGQA_EINVAL, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(HGQA_EINVAL, "workspace must be 16-byte aligned");
+    if (workspace_bytes < plan.workspace_bytes)
+      return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                  plan.workspace_bytes);
+  }
+  if ((long long)batch * plan.num_splits * l.Hkv > 0x7fffffffLL)
+    return fail(HGQA_EUNSUPPORTED, "too many decode blocks");
+  hgqa::DecodeArgs a{};
+  a.q = q;
+  a.gate = gate;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.B = batch;
+  a.Hq = l.Hq;
+  a.Hkv = l.Hkv;
+  a.G = l.G;
+  a.D = l.D;
+  a.cap = cache_capacity;
+  a.max_seq_len = max_seq_len;
+  a.sliding = l.sliding;
+  a.window = l.window;
+  a.split_keys = plan.split_keys;
+  a.num_splits = plan.num_splits;
+  a.scale = l.scale;
+  fill_rope(l, &a.rope);
+  hipError_t e = hgqa::launch_decode(a, l.elem, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(HGQA_EHIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
 
 extern "C" {
 
@@ -191,7 +286,8 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
   if (rc != HGQA_OK) return rc;
   if (batch < 0 || seq_len < 0) return fail(HGQA_EINVAL, "batch and seq_len must be >= 0");
   if (batch == 0 || seq_len == 0) return ok();
-  rc = check_prefill_call(l, batch, seq_len, q, k, v, gate, out, workspace, workspace_bytes);
+  rc = check_prefill_call(l, batch, seq_len, q, k, v, gate, out, workspace, workspace_bytes,
+                          prefill_ws(l, batch, seq_len));
   if (rc != HGQA_OK) return rc;
   hgqa::PrefillArgs a = prefill_args(l, batch, seq_len, q, k, v, gate, out, workspace);
   hipError_t e = hgqa::launch_prefill(a, l.elem, static_cast<hipStream_t>(stream));
@@ -200,32 +296,35 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
 }
 
 size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t n_new) {
-  return attn_prefill_workspace_bytes(layer, batch, n_new);
+  Layer l;
+  if (check_layer(layer, &l) != HGQA_OK || batch < 0 || n_new < 0) return 0;
+  return chunk_ws(l, batch, n_new);
 }
 
-int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new, int32_t start_pos,
-                       const void* q, const void* k, const void* v, const void* gate,
-                       void* k_cache, void* v_cache, int32_t cache_capacity, void* out,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
+                       const int32_t* start_pos, int32_t max_end_pos, const void* q,
+                       const void* k, const void* v, const void* gate, void* k_cache,
+                       void* v_cache, int32_t cache_capacity, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   Layer l;
   int rc = check_layer(layer, &l);
   if (rc != HGQA_OK) return rc;
-  if (batch < 0 || n_new < 0 || start_pos < 0)
-    return fail(HGQA_EINVAL, "batch, n_new and start_pos must be >= 0");
-  if ((long long)start_pos + n_new > 0x7fffffffLL)
-    return fail(HGQA_EUNSUPPORTED, "start_pos + n_new exceeds int32");
+  if (batch < 0 || n_new < 0) return fail(HGQA_EINVAL, "batch and n_new must be >= 0");
+  if (max_end_pos < n_new) return fail(HGQA_EINVAL, "max_end_pos must be >= n_new");
   if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
   if (l.sliding && cache_capacity != l.window)
     return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
                 l.window, cache_capacity);
-  if (!l.sliding && (long long)start_pos + n_new > cache_capacity)
-    return fail(HGQA_ENOSPACE, "positions up to %lld exceed the full cache capacity %d",
-                (long long)start_pos + n_new, cache_capacity);
+  if (!l.sliding && max_end_pos > cache_capacity)
+    return fail(HGQA_ENOSPACE, "max_end_pos %d exceeds the full cache capacity %d", max_end_pos,
+                cache_capacity);
   if (batch == 0 || n_new == 0) return ok();
-  rc = check_prefill_call(l, batch, n_new, q, k, v, gate, out, workspace, workspace_bytes);
+  rc = check_prefill_call(l, batch, n_new, q, k, v, gate, out, workspace, workspace_bytes,
+                          chunk_ws(l, batch, n_new));
   if (rc != HGQA_OK) return rc;
   if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
     return fail(HGQA_EUNSUPPORTED, "cache too large");
+  if (!start_pos) return fail(HGQA_EINVAL, "start_pos is NULL");
   if (!k_cache || !v_cache) return fail(HGQA_EINVAL, "a cache pointer is NULL");
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(HGQA_EINVAL, "the caches must be 16-byte aligned");
@@ -237,7 +336,9 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new, in
 
   // Attention first: a ring still holds the W - 1 positions before the chunk.
   hgqa::PrefillArgs a = prefill_args(l, batch, n_new, q, k, v, gate, out, workspace);
-  a.p0 = start_pos;
+  a.start_pos = start_pos;
+  a.max_end_pos = max_end_pos;
+  a.cs_bstride = (size_t)n_new * l.half;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.cap = cache_capacity;
@@ -248,8 +349,7 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new, in
 
   // Then the chunk joins the cache, as kv_append would leave it.
   hgqa::AppendArgs ap{};
-  ap.start_pos = nullptr;
-  ap.start_uniform = start_pos;
+  ap.start_pos = start_pos;
   ap.k_new = k;
   ap.v_new = v;
   ap.k_cache = k_cache;
@@ -309,12 +409,11 @@ int kv_append(const hgqa_layer* layer, int32_t batch, int32_t n_new, const int32
   return ok();
 }
 
-size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t max_seq_len,
-                                   int32_t cache_capacity) {
+size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t max_seq_len) {
   Layer l;
   if (check_layer(layer, &l) != HGQA_OK || batch < 1 || max_seq_len < 1) return 0;
-  (void)cache_capacity;
-  return hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len)
+  return hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len,
+                           g_decode_split_keys.load(std::memory_order_relaxed))
       .workspace_bytes;
 }
 
@@ -322,64 +421,24 @@ int attn_decode(const hgqa_layer* layer, int32_t batch, const void* q, const voi
                 const void* k_cache, const void* v_cache, int32_t cache_capacity,
                 const int32_t* seq_lens, int32_t max_seq_len, void* workspace,
                 size_t workspace_bytes, void* out, void* stream) {
-  Layer l;
-  int rc = check_layer(layer, &l);
-  if (rc != HGQA_OK) return rc;
-  if (batch < 0) return fail(HGQA_EINVAL, "batch must be >= 0");
-  if (batch == 0) return ok();
-  if (batch > 65535) return fail(HGQA_EUNSUPPORTED, "batch %d exceeds 65535", batch);
-  if (max_seq_len < 1) return fail(HGQA_EINVAL, "max_seq_len must be >= 1");
-  if (cache_capacity < 1) return fail(HGQA_EINVAL, "cache_capacity must be >= 1");
-  if (l.sliding && cache_capacity != l.window)
-    return fail(HGQA_EINVAL, "a sliding layer's ring must hold exactly W = %d slots (got %d)",
-                l.window, cache_capacity);
-  if (!l.sliding && max_seq_len > cache_capacity)
-    return fail(HGQA_ENOSPACE, "max_seq_len %d exceeds the full cache capacity %d", max_seq_len,
-                cache_capacity);
-  if (l.elem == hgqa::Elem::BF16 && l.G > 16)
-    return fail(HGQA_EUNSUPPORTED, "bf16 decode supports gqa_ratio <= 16 (got %d)", l.G);
-  if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
-    return fail(HGQA_EUNSUPPORTED, "cache too large");
-  if (!q || !gate || !k_cache || !v_cache || !seq_lens || !out)
-    return fail(HGQA_EINVAL, "a tensor pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(HGQA_EINVAL, "q, the caches and out must be 16-byte aligned");
-  if (out == q || out == gate) return fail(HGQA_EINVAL, "out must not alias an input");
-  const hgqa::DecodePlan plan =
-      hgqa::plan_decode(l.elem, batch, l.Hq, l.Hkv, l.D, l.sliding, l.window, max_seq_len);
-  if (plan.workspace_bytes > 0) {
-    if (!workspace) return fail(HGQA_EINVAL, "workspace is NULL");
-    if (!aligned16(workspace)) return fail(HGQA_EINVAL, "workspace must be 16-byte aligned");
-    if (workspace_bytes < plan.workspace_bytes)
-      return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                  plan.workspace_bytes);
+  return hgqa::decode_call(layer, batch, q, gate, k_cache, v_cache, cache_capacity, seq_lens,
+                           max_seq_len, workspace, workspace_bytes, out, stream, nullptr, 0);
+}
+
+int hgqa_set_tuning(int32_t knob, int32_t value) {
+  switch (knob) {
+    case HGQA_TUNE_PREFILL_WAVES:
+      if (value != 0 && value != 4 && value != 8)
+        return fail(HGQA_EINVAL, "HGQA_TUNE_PREFILL_WAVES takes 0, 4 or 8 (got %d)", value);
+      g_prefill_waves.store(value, std::memory_order_relaxed);
+      return ok();
+    case HGQA_TUNE_DECODE_SPLIT_KEYS:
+      if (value < 0) return fail(HGQA_EINVAL, "HGQA_TUNE_DECODE_SPLIT_KEYS must be >= 0");
+      g_decode_split_keys.store(value, std::memory_order_relaxed);
+      return ok();
+    default:
+      return fail(HGQA_EINVAL, "unknown tuning knob %d", knob);
   }
-  if ((long long)batch * plan.num_splits * l.Hkv > 0x7fffffffLL)
-    return fail(HGQA_EUNSUPPORTED, "too many decode blocks");
-  hgqa::DecodeArgs a{};
-  a.q = q;
-  a.gate = gate;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  a.partial = static_cast<float*>(workspace);
-  a.B = batch;
-  a.Hq = l.Hq;
-  a.Hkv = l.Hkv;
-  a.G = l.G;
-  a.D = l.D;
-  a.cap = cache_capacity;
-  a.max_seq_len = max_seq_len;
-  a.sliding = l.sliding;
-  a.window = l.window;
-  a.split_keys = plan.split_keys;
-  a.num_splits = plan.num_splits;
-  a.scale = l.scale;
-  fill_rope(l, &a.rope);
-  hipError_t e = hgqa::launch_decode(a, l.elem, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(HGQA_EHIP, "decode launch failed: %s", hipGetErrorString(e));
-  return ok();
 }
 
 }  // extern "C"

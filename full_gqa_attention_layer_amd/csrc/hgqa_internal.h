@@ -30,19 +30,31 @@ struct PrefillArgs {
   const void* gate;     // [B,T,Hq]
   void* out;            // [B,T,Hq,D]
   void* k_rot;          // workspace: [B,Hkv,T,D] rotated K
-  float2* cs_table;     // workspace: [T, half] (cos, sin)
+  float2* cs_table;     // workspace: [T, half] (cos, sin), or [B, T, half] for chunks
+  size_t cs_bstride;    // float2 entries between sequences' tables (0: one shared table)
   int B, T, Hq, Hkv, G, D;
   int sliding, window;
   float scale;          // softmax scale
   RopeArgs rope;
-  // Chunked prefill: row t of this call sits at absolute position p0 + t, and
-  // keys at positions < p0 come from the layer's cache ([B,Hkv,cap,D], K
-  // rotated; slot p, or p mod cap for a ring). Plain prefill: p0 = 0, no cache.
-  int p0;
+  // Chunked prefill: row t of sequence b sits at absolute position
+  // p0(b) + t, p0(b) = start_pos[b] clamped to [0, max_end_pos - T], and keys
+  // at positions < p0(b) come from the layer's cache ([B,Hkv,cap,D], K
+  // rotated; slot p, or p mod cap for a ring). Plain prefill: start_pos NULL
+  // (p0 = 0), no cache.
+  const int32_t* start_pos;
+  int max_end_pos;
   const void* k_cache;
   const void* v_cache;
   int cap, ring;
+  int waves;            // bf16 workgroup shape override: 0 automatic, 4 or 8
 };
+
+// Start position of sequence b in a prefill call (device side).
+__device__ __forceinline__ int prefill_p0(const PrefillArgs& a, int b) {
+  if (!a.start_pos) return 0;
+  const int p = a.start_pos[b];
+  return p < 0 ? 0 : (p > a.max_end_pos - a.T ? a.max_end_pos - a.T : p);
+}
 
 // Rotated-K and cos/sin-table pre-pass, then the attention kernel.
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s);
@@ -83,8 +95,19 @@ struct DecodePlan {
   int num_splits;
   size_t workspace_bytes;
 };
+// split_keys_override > 0 fixes the keys per split (tuning only).
 DecodePlan plan_decode(Elem e, int B, int Hq, int Hkv, int D, int sliding,
-                       int window, int max_seq_len);
+                       int window, int max_seq_len, int split_keys_override);
 hipError_t launch_decode(const DecodeArgs& a, Elem e, hipStream_t s);
+
+// The checks, split plan and launch behind attn_decode. With scratch_fn set,
+// the per-split partials go to the buffer it returns for the stream's GPU
+// (scratch_bytes long) instead of the caller's workspace.
+typedef hipError_t (*ScratchFn)(hipStream_t stream, void** ptr);
+int decode_call(const void* layer, int batch, const void* q, const void* gate,
+                const void* k_cache, const void* v_cache, int cache_capacity,
+                const int32_t* seq_lens, int max_seq_len, void* workspace,
+                size_t workspace_bytes, void* out, void* stream, ScratchFn scratch_fn,
+                size_t scratch_bytes);
 
 }  // namespace hgqa

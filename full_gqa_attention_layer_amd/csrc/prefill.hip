@@ -24,7 +24,6 @@
 // tiles that cross the diagonal or the window edge are masked elementwise.
 #include "device_util.h"
 
-#include <cstdlib>
 #include <type_traits>
 
 namespace hgqa {
@@ -138,8 +137,8 @@ struct PrefillLds {
 
 // kCache: chunked prefill, keys before position p0 come from the cache.
 // KW: waves per workgroup (4: two workgroups per CU; 8: one, every K/V tile
-// serving twice the rows).
-template <int D, bool kCache, int KW>
+// serving twice the rows). SL: sliding-window mask (else causal only).
+template <int D, bool kCache, int KW, bool SL>
 __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int kWaves = KW;
   constexpr int kRows = kWaves * kRowsPerWave;  // query rows per workgroup
@@ -198,7 +197,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const int t_hi = t0 + pos_of_local(nrows - 1);
   // Masks and key ranges use absolute positions: row t of this call sits at
   // p0 + t, and so does key t of this call.
-  const int p0 = kCache ? a.p0 : 0;
+  const int p0 = kCache ? prefill_p0(a, b) : 0;
   const int tw_lo = p0 + t0 + pos_of_local(min(wave * kRowsPerWave, nrows - 1));
   const int tw_hi = p0 + t0 + pos_of_local(min(wave * kRowsPerWave + kRowsPerWave - 1, nrows - 1));
   const int t_abs = p0 + t_row;
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const size_t blk_row = (size_t)(b * T + t0) * Hq + kvh * G;
 
   // ---- key range of the workgroup (absolute positions)
-  const int j_lo = a.sliding ? max(0, p0 + t_lo - a.window + 1) : 0;
+  const int j_lo = SL ? max(0, p0 + t_lo - a.window + 1) : 0;
   const int ntiles = (p0 + t_hi + 1 - j_lo + kBN - 1) / kBN;
   const int j_last = p0 + T - 1;
 
@@ -316,10 +315,11 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   // ---- cos/sin rows of the workgroup's positions go to LDS when they fit;
   // else Q reads them from the global table.
   const int half = a.rope.half, rdims = a.rope.rdims;
+  const float2* cs_seq = a.cs_table + (size_t)b * a.cs_bstride;  // this sequence's rows
   const int cs_bytes = (t_hi - t_lo + 1) * half * 8;
   const bool cs_lds = half > 0 && cs_bytes <= (int)sizeof(sm.cs);
   if (cs_lds) {
-    const char* src0 = reinterpret_cast<const char*>(a.cs_table + (size_t)t_lo * half);
+    const char* src0 = reinterpret_cast<const char*>(cs_seq + (size_t)t_lo * half);
     const int nblk = (cs_bytes + 1023) / 1024;
     for (int I = wave; I < nblk; I += kWaves) {
       const int off = min(1024 * I + 16 * lane, cs_bytes - 16);
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   } else if (half % 16 == 0) {
     // The RoPE partner of every chunk sits in this lane, half/16 chunks away.
     const float2* csl = sm.cs + dt_row * half;
-    const float2* csg = a.cs_table + (size_t)t_row * half;
+    const float2* csg = cs_seq + (size_t)t_row * half;
     switch (half / 16) {
 #define HGQA_ROPE_CASE(H)                                 \
   case H:                                                 \
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     }
   } else {
     // r/2 an odd multiple of 8: partner chunks are read again from HBM.
-    const float2* csrow = a.cs_table + (size_t)t_row * half;
+    const float2* csrow = cs_seq + (size_t)t_row * half;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int d0 = 16 * s + 8 * g;
@@ -449,13 +449,12 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     }
 
     // mask only where the tile crosses the diagonal or the window edge
-    const bool need_mask = (j0 + kBN - 1 > tw_lo) ||
-                           (a.sliding && j0 < tw_hi - a.window + 1);
+    const bool need_mask = (j0 + kBN - 1 > tw_lo) || (SL && j0 < tw_hi - a.window + 1);
     if (need_mask) {
       // key j = j0 + 4g + off is visible iff 0 <= t_row - j < W (W = 2^31 when
       // full): one unsigned compare per element against a per-lane base.
       const int base = t_abs - j0 - 4 * g;
-      const unsigned wlim = a.sliding ? (unsigned)a.window : 0x80000000u;
+      const unsigned wlim = SL ? (unsigned)a.window : 0x80000000u;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -590,7 +589,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   const int kvh = h / a.G;
   const int half = a.rope.half, rdims = a.rope.rdims;
   const float* q = static_cast<const float*>(a.q) + id * D;
-  const float2* cs = a.cs_table + (size_t)t * half;
+  const float2* cs = a.cs_table + (size_t)b * a.cs_bstride + (size_t)t * half;
   for (int d = lane; d < D; d += 64) {
     float x = q[d];
     if (d < half) x = fmaf(x, cs[d].x, -q[d + half] * cs[d].y);
@@ -600,7 +599,7 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   __syncthreads();
   // Absolute positions: row t sits at p0 + t; keys before p0 (a chunk that
   // continues a cached sequence) come from the cache, slot j or j mod cap.
-  const int p0 = a.p0, ta = p0 + t;
+  const int p0 = prefill_p0(a, b), ta = p0 + t;
   const int lo = a.sliding ? max(0, ta - a.window + 1) : 0;
   const float* kr = static_cast<const float*>(a.k_rot) + (size_t)(b * a.Hkv + kvh) * T * D;
   const float* v = static_cast<const float*>(a.v) + ((size_t)b * T * a.Hkv + kvh) * D;
@@ -655,16 +654,21 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
 // for short windows, where a workgroup's fixed costs weigh more and two
 // workgroups per CU hide them (W = 512: 8 waves is 9% slower), and for
 // chunks of fewer than 2048 rows (a few new tokens would leave most of 256
-// rows empty). D = 128 only. HGQA_PREFILL_WAVES=4|8 overrides (tuning only).
+// rows empty). D = 128 only; a.waves (4 or 8) overrides the choice.
 static int prefill_waves(const PrefillArgs& a) {
+  if (a.D != 128) return 4;
+  if (a.waves == 4 || a.waves == 8) return a.waves;
   const bool long_span = !a.sliding || a.window >= 1024;
   const bool enough_rows = a.k_cache == nullptr || (long long)a.T * a.G >= 2048;
-  int kw = (a.D == 128 && long_span && enough_rows) ? 8 : 4;
-  if (const char* env = getenv("HGQA_PREFILL_WAVES")) {
-    const int v = atoi(env);
-    if ((v == 4 || v == 8) && a.D == 128) kw = v;
-  }
-  return kw;
+  return long_span && enough_rows ? 8 : 4;
+}
+
+template <int D, bool kCache, int KW>
+static void launch_bf16(const PrefillArgs& a, dim3 grid, hipStream_t s) {
+  if (a.sliding)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, kCache, KW, true>), grid, dim3(KW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, kCache, KW, false>), grid, dim3(KW * 64), 0, s, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
@@ -680,15 +684,15 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const int kw = prefill_waves(a);
   const long long rows = (long long)kw * kRowsPerWave;
   const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv;
-  const dim3 grid((unsigned)blocks), block(kw * 64);
+  const dim3 grid((unsigned)blocks);
   if (a.D == 128) {
-    if (cache && kw == 8) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 8>), grid, block, 0, s, a);
-    else if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<128, true, 4>), grid, block, 0, s, a);
-    else if (kw == 8) hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false, 4>), grid, block, 0, s, a);
+    if (cache && kw == 8) launch_bf16<128, true, 8>(a, grid, s);
+    else if (cache) launch_bf16<128, true, 4>(a, grid, s);
+    else if (kw == 8) launch_bf16<128, false, 8>(a, grid, s);
+    else launch_bf16<128, false, 4>(a, grid, s);
   } else {
-    if (cache) hipLaunchKernelGGL((prefill_bf16_kernel<64, true, 4>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false, 4>), grid, block, 0, s, a);
+    if (cache) launch_bf16<64, true, 4>(a, grid, s);
+    else launch_bf16<64, false, 4>(a, grid, s);
   }
   return hipGetLastError();
 }

@@ -1,8 +1,9 @@
 // RoPE kernels that touch each key once:
 //  * the prefill pre-pass: rotates K into a head-major copy [B,Hkv,T,D] and
 //    writes the (cos, sin) table [T, r/2] that the attention kernel uses to
-//    rotate Q while loading it; row t sits at absolute position p0 + t (p0 > 0
-//    for a chunk that continues a cached sequence);
+//    rotate Q while loading it; row t of sequence b sits at absolute position
+//    p0(b) + t (p0(b) > 0 for a chunk that continues a cached sequence, and
+//    then each sequence gets its own table);
 //  * kv_append: rotates new keys at their absolute positions and scatters
 //    keys and values into the layer's cache, slot p (full layer) or p mod W
 //    (sliding layer ring).
@@ -52,11 +53,16 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass(PrefillArgs a) {
   const int t0 = blockIdx.x * kPrepassPositions;
   const int np = min(kPrepassPositions, a.T - t0);
   const int half = a.rope.half;
+  const int p0 = prefill_p0(a, b);
+  // one table for every sequence of a plain prefill (sequence 0 writes it),
+  // one per sequence for a chunk
+  const bool write_cs = a.cs_bstride != 0 || b == 0;
+  float2* cs_out = a.cs_table + (size_t)b * a.cs_bstride;
   for (int e = threadIdx.x; e < np * half; e += blockDim.x) {
     int tp = e / half, i = e - tp * half;
-    float2 c = rope_cos_sin(a.p0 + t0 + tp, a.rope.freq_over_pi[i]);
+    float2 c = rope_cos_sin(p0 + t0 + tp, a.rope.freq_over_pi[i]);
     cs[tp][i] = c;
-    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
+    if (write_cs) cs_out[(size_t)(t0 + tp) * half + i] = c;
   }
   __syncthreads();
   const T* k = static_cast<const T*>(a.k);
@@ -123,11 +129,14 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
     praw[c] = *reinterpret_cast<const u32x4_t*>(row + partner(d0));
   }
 
+  const int p0 = prefill_p0(a, b);
+  const bool write_cs = a.cs_bstride != 0 || b == 0;  // see prefill_rope_prepass
+  float2* cs_out = a.cs_table + (size_t)b * a.cs_bstride;
   auto trig = [&](int e, double f) {
     const int tp = e / half, i = e - tp * half;
-    const float2 c = rope_cos_sin(a.p0 + t0 + tp, f);
+    const float2 c = rope_cos_sin(p0 + t0 + tp, f);
     cs[tp][i] = c;
-    if (b == 0) a.cs_table[(size_t)(t0 + tp) * half + i] = c;
+    if (write_cs) cs_out[(size_t)(t0 + tp) * half + i] = c;
   };
   if (e0 < ntrig) trig(e0, f0);
   if (e1 < ntrig) trig(e1, f1);

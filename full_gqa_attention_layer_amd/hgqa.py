@@ -1,9 +1,11 @@
 """Python binding of libhgqa.so: the C ABI of include/hgqa.h under the same names.
 
-This module only marshals arguments: it checks tensor shapes, dtypes and
-devices, allocates outputs and workspaces with torch, and passes raw device
-pointers and the current HIP stream. Every step of the computation runs in
-the library's HIP kernels. If the library is missing, every call raises.
+This module only marshals arguments: it checks every tensor's shape against
+the layer descriptor (Hq, Hkv = Hq / G and D come from the descriptor, never
+from the tensors), its dtype and device, allocates outputs and workspaces with
+torch, and passes raw device pointers and the current HIP stream. Every step
+of the computation runs in the library's HIP kernels. If the library is
+missing, every call raises.
 """
 from __future__ import annotations
 
@@ -12,17 +14,16 @@ import os
 
 import torch
 
-# HGQA_LIBRARY may name another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("HGQA_LIBRARY") or os.path.join(
-    os.path.dirname(os.path.abspath(__file__)), "libhgqa.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhgqa.so")
 
 FULL, SLIDING = 0, 1
 BF16, FP32 = 0, 1
 OK, EINVAL, EUNSUPPORTED, ENOSPACE, EHIP = 0, -1, -2, -3, -4
+TUNE_PREFILL_WAVES, TUNE_DECODE_SPLIT_KEYS = 1, 2
 
 EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "attn_prefill_chunk_workspace_bytes",
             "attn_prefill_chunk", "kv_append", "attn_decode_workspace_bytes", "attn_decode",
-            "hgqa_last_error")
+            "hgqa_set_tuning", "hgqa_last_error")
 
 
 class HgqaLayer(ctypes.Structure):
@@ -62,14 +63,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_prefill.restype = ctypes.c_int
     lib.attn_prefill_chunk_workspace_bytes.argtypes = [LP, I, I]
     lib.attn_prefill_chunk_workspace_bytes.restype = S
-    lib.attn_prefill_chunk.argtypes = [LP, I, I, I, P, P, P, P, P, P, I, P, P, S, P]
+    lib.attn_prefill_chunk.argtypes = [LP, I, I, P, I, P, P, P, P, P, P, I, P, P, S, P]
     lib.attn_prefill_chunk.restype = ctypes.c_int
     lib.kv_append.argtypes = [LP, I, I, P, I, P, P, P, P, I, P]
     lib.kv_append.restype = ctypes.c_int
-    lib.attn_decode_workspace_bytes.argtypes = [LP, I, I, I]
+    lib.attn_decode_workspace_bytes.argtypes = [LP, I, I]
     lib.attn_decode_workspace_bytes.restype = S
     lib.attn_decode.argtypes = [LP, I, P, P, P, P, I, P, I, P, S, P, P]
     lib.attn_decode.restype = ctypes.c_int
+    lib.hgqa_set_tuning.argtypes = [I, I]
+    lib.hgqa_set_tuning.restype = ctypes.c_int
     lib.hgqa_last_error.argtypes = []
     lib.hgqa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -114,11 +117,13 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _need(t, name, shape, dtype):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if t.dtype != dtype:
@@ -127,28 +132,49 @@ def _need(t, name, shape, dtype):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _on_gpu(**tensors):
+    """After every shape is checked: each tensor must live on the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+
+
 def attn_prefill_workspace_bytes(L: HgqaLayer, batch: int, seq_len: int) -> int:
     return int(load_library().attn_prefill_workspace_bytes(ctypes.byref(L), batch, seq_len))
+
+
+def _heads(L: HgqaLayer):
+    """(Hq, Hkv, D) as the descriptor gives them; the library indexes with these."""
+    if L.gqa_ratio < 1 or L.num_q_heads < 1 or L.num_q_heads % L.gqa_ratio:
+        raise ValueError(f"num_q_heads {L.num_q_heads} is not a positive multiple of "
+                         f"gqa_ratio {L.gqa_ratio}")
+    return L.num_q_heads, L.num_q_heads // L.gqa_ratio, L.head_dim
+
+
+def set_tuning(knob: int, value: int):
+    """Tuning override for tests and measurements (hgqa_set_tuning); 0 = automatic."""
+    _check(load_library().hgqa_set_tuning(int(knob), int(value)))
 
 
 def attn_prefill(L: HgqaLayer, q, k, v, gate, out=None, workspace=None):
     """Gated causal/sliding GQA of a prompt at positions 0..T-1 (see hgqa.h)."""
     lib = load_library()
-    B, T, Hq, D = q.shape
-    Hkv = Hq // max(L.gqa_ratio, 1)
+    Hq, Hkv, D = _heads(L)
+    B, T = q.shape[:2]
     dt = _torch_dtype(L)
-    _need(q, "q", (B, T, L.num_q_heads, L.head_dim), dt)
+    _need(q, "q", (B, T, Hq, D), dt)
     _need(k, "k", (B, T, Hkv, D), dt)
     _need(v, "v", (B, T, Hkv, D), dt)
     _need(gate, "gate", (B, T, Hq), dt)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", (B, T, Hq, D), dt)
+    _on_gpu(q=q, k=k, v=v, gate=gate, out=out, workspace=workspace)
     need = attn_prefill_workspace_bytes(L, B, T)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.attn_prefill(ctypes.byref(L), B, T, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
-                            _ptr(out), _ptr(workspace), workspace.numel(), _stream()))
+                            _ptr(out), _ptr(workspace), _nbytes(workspace), _stream()))
     return out
 
 
@@ -156,36 +182,49 @@ def attn_prefill_chunk_workspace_bytes(L: HgqaLayer, batch: int, n_new: int) -> 
     return int(load_library().attn_prefill_chunk_workspace_bytes(ctypes.byref(L), batch, n_new))
 
 
-def attn_prefill_chunk(L: HgqaLayer, start_pos: int, q, k, v, gate, k_cache, v_cache,
-                       out=None, workspace=None):
-    """New tokens at start_pos.. over the cache and themselves, then appended (see hgqa.h)."""
+def attn_prefill_chunk(L: HgqaLayer, start_pos, q, k, v, gate, k_cache, v_cache,
+                       max_end_pos=None, out=None, workspace=None):
+    """New tokens of sequence b at start_pos[b].. over the cache and themselves, then
+    appended (see hgqa.h). start_pos: an int (every sequence) or an int32 tensor [B] on
+    the GPU, which then needs max_end_pos (>= start_pos[b] + n for every b)."""
     lib = load_library()
-    B, n, Hq, D = q.shape
-    Hkv = Hq // max(L.gqa_ratio, 1)
+    Hq, Hkv, D = _heads(L)
+    B, n = q.shape[:2]
     cap = k_cache.shape[2]
     dt = _torch_dtype(L)
-    _need(q, "q", (B, n, L.num_q_heads, L.head_dim), dt)
+    if isinstance(start_pos, int):
+        if max_end_pos is None:
+            max_end_pos = start_pos + n
+        start_pos = torch.full((B,), start_pos, dtype=torch.int32, device=q.device)
+    elif max_end_pos is None:
+        raise ValueError("a start_pos tensor needs max_end_pos")
+    _need(q, "q", (B, n, Hq, D), dt)
     _need(k, "k", (B, n, Hkv, D), dt)
     _need(v, "v", (B, n, Hkv, D), dt)
     _need(gate, "gate", (B, n, Hq), dt)
     _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
     _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    _need(start_pos, "start_pos", (B,), torch.int32)
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", (B, n, Hq, D), dt)
+    _on_gpu(start_pos=start_pos, q=q, k=k, v=v, gate=gate, k_cache=k_cache, v_cache=v_cache,
+            out=out, workspace=workspace)
     need = attn_prefill_chunk_workspace_bytes(L, B, n)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib.attn_prefill_chunk(ctypes.byref(L), B, n, int(start_pos), _ptr(q), _ptr(k), _ptr(v),
-                                  _ptr(gate), _ptr(k_cache), _ptr(v_cache), cap, _ptr(out),
-                                  _ptr(workspace), workspace.numel(), _stream()))
+    _check(lib.attn_prefill_chunk(ctypes.byref(L), B, n, _ptr(start_pos), int(max_end_pos),
+                                  _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(k_cache),
+                                  _ptr(v_cache), cap, _ptr(out), _ptr(workspace),
+                                  _nbytes(workspace), _stream()))
     return out
 
 
 def kv_append(L: HgqaLayer, start_pos, max_end_pos: int, k_new, v_new, k_cache, v_cache):
     """Rotate and scatter new K/V into the layer's cache (see hgqa.h)."""
     lib = load_library()
-    B, n, Hkv, D = k_new.shape
+    _, Hkv, D = _heads(L)
+    B, n = k_new.shape[:2]
     cap = k_cache.shape[2]
     dt = _torch_dtype(L)
     _need(start_pos, "start_pos", (B,), torch.int32)
@@ -193,24 +232,24 @@ def kv_append(L: HgqaLayer, start_pos, max_end_pos: int, k_new, v_new, k_cache, 
     _need(v_new, "v_new", (B, n, Hkv, D), dt)
     _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
     _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    _on_gpu(start_pos=start_pos, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
     _check(lib.kv_append(ctypes.byref(L), B, n, _ptr(start_pos), int(max_end_pos), _ptr(k_new),
                          _ptr(v_new), _ptr(k_cache), _ptr(v_cache), cap, _stream()))
 
 
-def attn_decode_workspace_bytes(L: HgqaLayer, batch: int, max_seq_len: int,
-                                cache_capacity: int) -> int:
-    return int(load_library().attn_decode_workspace_bytes(ctypes.byref(L), batch, max_seq_len,
-                                                          cache_capacity))
+def attn_decode_workspace_bytes(L: HgqaLayer, batch: int, max_seq_len: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(ctypes.byref(L), batch, max_seq_len))
 
 
 def attn_decode(L: HgqaLayer, q, gate, k_cache, v_cache, seq_lens, max_seq_len: int,
                 out=None, workspace=None):
     """One query token per sequence against its cache (see hgqa.h)."""
     lib = load_library()
-    B, Hq, D = q.shape
-    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    Hq, Hkv, D = _heads(L)
+    B = q.shape[0]
+    cap = k_cache.shape[2]
     dt = _torch_dtype(L)
-    _need(q, "q", (B, L.num_q_heads, L.head_dim), dt)
+    _need(q, "q", (B, Hq, D), dt)
     _need(gate, "gate", (B, Hq), dt)
     _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
     _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
@@ -218,11 +257,12 @@ def attn_decode(L: HgqaLayer, q, gate, k_cache, v_cache, seq_lens, max_seq_len: 
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", (B, Hq, D), dt)
-    need = attn_decode_workspace_bytes(L, B, max_seq_len, cap)
+    _on_gpu(q=q, gate=gate, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, out=out,
+            workspace=workspace)
+    need = attn_decode_workspace_bytes(L, B, max_seq_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.attn_decode(ctypes.byref(L), B, _ptr(q), _ptr(gate), _ptr(k_cache),
                            _ptr(v_cache), cap, _ptr(seq_lens), int(max_seq_len),
-                           _ptr(workspace), ws_bytes, _ptr(out), _stream()))
+                           _ptr(workspace), _nbytes(workspace), _ptr(out), _stream()))
     return out

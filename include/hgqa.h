@@ -38,8 +38,11 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the legacy default
  *     stream) and the call returns without waiting for it.
  *   - The library allocates no device memory and keeps no state between calls
- *     besides a per-thread error message. Scratch memory is passed in by the
- *     caller as `workspace`, sized by the matching *_workspace_bytes query.
+ *     besides a per-thread error message and the process-wide tuning
+ *     overrides of hgqa_set_tuning. Scratch memory is passed in by the caller
+ *     as `workspace`, sized by the matching *_workspace_bytes query: prefill
+ *     keeps each key rotated once there (and the cos/sin rows the queries
+ *     are rotated with), decode keeps its per-split partial results.
  *   - Device-side integers (start_pos, seq_lens) are trusted within the
  *     host-side bounds passed with them; values outside are clamped so that
  *     no access leaves the buffers, and the result for them is unspecified.
@@ -138,43 +141,52 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len,
                  void* stream);
 
 /*
- * Scratch bytes attn_prefill_chunk needs: the same as attn_prefill for a
- * prompt of n_new tokens.
+ * Scratch bytes attn_prefill_chunk needs: the rotated new keys
+ * [B, Hkv, n_new, D] in the layer dtype and one cos/sin table per sequence
+ * [B, n_new, r/2] of float pairs (the sequences start at different
+ * positions), each part rounded up to 256 bytes. Returns 0 for an invalid
+ * layer.
  */
 size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch,
                                           int32_t n_new);
 
 /*
- * Chunked prefill: n_new new tokens per sequence, at absolute positions
- * start_pos .. start_pos + n_new - 1, attend over the layer's cache (the
- * positions before start_pos) and over themselves; then they are appended to
- * the cache. The result is what attn_prefill over the whole sequence gives for
- * these rows. The cache-backed prefill the model pages leave to the full
- * implementation ("Step-3.7-Flash-oQ3e" walkthrough, section 6) and the
- * sliding cache of section 2.2 of the same page.
- *   start_pos [host]      same for every sequence, >= 0
+ * Chunked prefill: the n_new new tokens of sequence b, at absolute positions
+ * start_pos[b] .. start_pos[b] + n_new - 1, attend over the layer's cache (the
+ * positions before start_pos[b]) and over themselves; then they are appended
+ * to the cache. The result is what attn_prefill over the whole sequence gives
+ * for these rows. This is the cache-backed prefill that the model pages leave
+ * to the full implementation ("Step-3.7-Flash-oQ3e" walkthrough, section 6,
+ * where the model class takes over KV-cache prefill control) over the
+ * sliding cache of section 2.2 of the same page. A multi-token decode step
+ * (one token plus draft tokens, each seeing the cache and the earlier new
+ * tokens; the "Step-3.7-Flash" model card lists num_nextn_predict_layers 3)
+ * is this call with a small n_new; every sequence may sit at its own
+ * position.
+ *   start_pos [B] int32   position of the first new token of each sequence
+ *   max_end_pos [host]    >= start_pos[b] + n_new for every b, >= n_new
  *   q     [B, n, Hq, D]   queries, not rotated
  *   k, v  [B, n, Hkv, D]  new keys (not rotated) and values
  *   gate  [B, n, Hq]      gate logits
  *   k_cache, v_cache [B, Hkv, cap, D]  as kv_append fills them: rotated keys
- *         and values of positions < start_pos. Full layer: slot p holds
- *         position p, and cap >= start_pos + n. Sliding layer: cap == W and
+ *         and values of positions < start_pos[b]. Full layer: slot p holds
+ *         position p, and cap >= max_end_pos. Sliding layer: cap == W and
  *         slot p mod W holds position p for the last W positions before
- *         start_pos (every earlier position the new rows can see).
+ *         start_pos[b] (every earlier position the new rows can see).
  *   out   [B, n, Hq, D]   gated attention output
  *   workspace            >= attn_prefill_chunk_workspace_bytes(layer, B, n)
  * In stream order the attention reads the cache before the append writes it,
  * so a ring may be overwritten by its own chunk. The caches must not alias any
- * other argument. n_new == 0 or batch == 0 does nothing. A multi-token decode
- * step (one token plus draft tokens, each seeing the cache and the earlier new
- * tokens) is this call with a small n_new. Errors: as attn_prefill, plus
- * HGQA_ENOSPACE when a full cache is too small and HGQA_EINVAL when a ring's
- * capacity differs from W.
+ * other argument. n_new == 0 or batch == 0 does nothing. Errors: as
+ * attn_prefill, plus HGQA_ENOSPACE when a full cache is smaller than
+ * max_end_pos and HGQA_EINVAL when a ring's capacity differs from W. A
+ * start_pos[b] outside [0, max_end_pos - n_new] is clamped into it (no access
+ * leaves the buffers; that sequence's result is unspecified).
  */
 int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
-                       int32_t start_pos, const void* q, const void* k, const void* v,
-                       const void* gate, void* k_cache, void* v_cache,
-                       int32_t cache_capacity, void* out, void* workspace,
+                       const int32_t* start_pos, int32_t max_end_pos, const void* q,
+                       const void* k, const void* v, const void* gate, void* k_cache,
+                       void* v_cache, int32_t cache_capacity, void* out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 /*
@@ -199,13 +211,19 @@ int kv_append(const hgqa_layer* layer, int32_t batch, int32_t n_new,
 /*
  * Scratch bytes attn_decode needs: per-split partial results (running max,
  * running sum and unnormalised output, float32) for the split count the
- * library picks for this shape. May be 0 when no split is needed.
+ * library picks for this layer, batch and longest context. May be 0 when no
+ * split is needed. Returns 0 for an invalid layer.
  */
 size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch,
-                                   int32_t max_seq_len, int32_t cache_capacity);
+                                   int32_t max_seq_len);
 
 /*
- * Decode: one new query token per sequence against its cache.
+ * Decode: one new query token per sequence against its cache. This is the
+ * cached form of the layer that "Step-3.7-Flash-oQ3e" walkthrough 2.2
+ * describes: a sliding layer's cache keeps only the last W tokens and the
+ * query attends to them, a full layer's cache keeps every token (2.3 of the
+ * same page: full layers see the whole context). RoPE and the per-head
+ * sigmoid gate follow 2.3.
  *   q        [B, Hq, D]  queries, not rotated; the query of sequence b sits
  *                        at position seq_lens[b] - 1
  *   gate     [B, Hq]     gate logits
@@ -214,15 +232,32 @@ size_t attn_decode_workspace_bytes(const hgqa_layer* layer, int32_t batch,
  *   seq_lens [B] int32   tokens in the cache including the new one, >= 1
  *   max_seq_len [host]   >= every seq_lens[b]; full layers need
  *                        cache_capacity >= max_seq_len
+ *   workspace            >= attn_decode_workspace_bytes(layer, B,
+ *                        max_seq_len) bytes (may be NULL when that is 0)
  *   out      [B, Hq, D]
  * A full layer attends to slots 0..L-1; a sliding layer's ring holds the
- * last min(L, W) positions and the query attends to all of them.
+ * last min(L, W) positions and the query attends to all of them. bf16
+ * layers support gqa_ratio <= 16 (HGQA_EUNSUPPORTED above). A seq_lens[b]
+ * outside [1, max_seq_len] is clamped into it.
  */
 int attn_decode(const hgqa_layer* layer, int32_t batch, const void* q,
                 const void* gate, const void* k_cache, const void* v_cache,
                 int32_t cache_capacity, const int32_t* seq_lens,
                 int32_t max_seq_len, void* workspace, size_t workspace_bytes,
                 void* out, void* stream);
+
+/*
+ * Tuning overrides, for tests and measurements only: process-wide settings
+ * that later calls read when they plan their launches. value 0 restores the
+ * library's own choice.
+ *   HGQA_TUNE_PREFILL_WAVES      4 or 8 waves per bf16 prefill workgroup
+ *                                (head_dim 128 only; other layers ignore it)
+ *   HGQA_TUNE_DECODE_SPLIT_KEYS  keys per decode split (rounded up to 32)
+ * Returns HGQA_EINVAL for an unknown knob or value. Changing a knob while
+ * another thread is inside a call gives that call either setting.
+ */
+enum { HGQA_TUNE_PREFILL_WAVES = 1, HGQA_TUNE_DECODE_SPLIT_KEYS = 2 };
+int hgqa_set_tuning(int32_t knob, int32_t value);
 
 /* Text of the last error returned on the calling thread ("" if none). */
 const char* hgqa_last_error(void);

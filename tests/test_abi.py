@@ -109,25 +109,35 @@ def test_prefill_workspace_formula(lib):
 
 
 def test_prefill_chunk_argument_checks(lib):
-    p, o, c1, c2 = (ctypes.c_void_p(x) for x in (256, 4096, 8192, 12288))
+    p, o, c1, c2, sp = (ctypes.c_void_p(x) for x in (256, 4096, 8192, 12288, 16384))
     ws = 1 << 30
 
-    def call(L, B=1, n=4, p0=10, cap=512, kc=c1, vc=c2, wsb=ws):
-        return lib.attn_prefill_chunk(ctypes.byref(L), B, n, p0, p, p, p, p, kc, vc, cap, o, p,
-                                      wsb, None)
+    def call(L, B=1, n=4, start=sp, end=14, cap=512, kc=c1, vc=c2, wsb=ws):
+        return lib.attn_prefill_chunk(ctypes.byref(L), B, n, start, end, p, p, p, p, kc, vc, cap,
+                                      o, p, wsb, None)
     Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
     Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
     assert call(Ls, cap=256) == hgqa.EINVAL          # a ring holds exactly W slots
-    assert call(Lf, cap=13) == hgqa.ENOSPACE          # 10 + 4 positions need 14 slots
-    assert call(Lf, p0=-1) == hgqa.EINVAL
+    assert call(Lf, cap=13) == hgqa.ENOSPACE          # positions up to 14 need 14 slots
+    assert call(Lf, end=3) == hgqa.EINVAL             # max_end_pos below n_new
     assert call(Lf, n=0) == hgqa.OK                   # nothing to do
     assert call(Lf, B=0) == hgqa.OK
+    assert call(Lf, start=ctypes.c_void_p(0)) == hgqa.EINVAL
     assert call(Lf, kc=c1, vc=c1) == hgqa.EINVAL      # the caches must differ
     assert call(Lf, kc=o) == hgqa.EINVAL              # a cache must not alias out
     assert call(Lf, kc=ctypes.c_void_p(0)) == hgqa.EINVAL
     assert call(Lf, wsb=1) == hgqa.ENOSPACE
-    assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), 2, 100) == \
-        lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 2, 100)
+
+
+def test_prefill_chunk_workspace_formula(lib):
+    """Rotated new keys [B,Hkv,n,D] and one cos/sin table per sequence
+    [B,n,r/2] (each sequence starts at its own position), each rounded up to
+    256 bytes."""
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, n in ((1, 2048), (64, 4), (3, 7)):
+        want = r256(B * 8 * n * 128 * 2) + r256(B * n * 32 * 8)
+        assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), B, n) == want
 
 
 def test_kv_append_argument_checks(lib):
@@ -146,7 +156,7 @@ def test_kv_append_argument_checks(lib):
 def test_decode_argument_checks(lib):
     p = ctypes.c_void_p(256)
     Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
-    ws = lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072, 131072)
+    ws = lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072)
     assert ws > 0
     o = ctypes.c_void_p(4096)
     args = lambda cap, mx, wsb: (ctypes.byref(Lf), 64, p, p, p, p, cap, p, mx, p, wsb, o, None)
@@ -171,10 +181,62 @@ def test_decode_split_plan(lib):
     split, and a lone short batch many splits of 128 keys."""
     Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
     per_split = 64 * (128 + 2) * 4                      # one sequence, all heads
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072, 131072) == \
-        64 * 4 * per_split
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072) == 64 * 4 * per_split
     Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(Ls), 64, 131072, 512) == 0
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Ls), 64, 131072) == 0
     # 8 (sequence, KV head) pairs: aim for 2048 workgroups, at least 128 keys each
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000, 20000) == \
-        1 * 157 * per_split
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 1 * 157 * per_split
+
+
+def test_tuning_overrides(lib):
+    """hgqa_set_tuning: the split override shows in the decode workspace; bad
+    knobs and values are rejected; 0 restores the automatic plan."""
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    per_split = 64 * (128 + 2) * 4
+    try:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 1000) == hgqa.OK  # -> 1024 keys
+        assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 20 * per_split
+        assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 1 << 20) == hgqa.OK
+        assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 0  # one split
+    finally:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 0) == hgqa.OK
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 157 * per_split
+    assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, -1) == hgqa.EINVAL
+    assert lib.hgqa_set_tuning(hgqa.TUNE_PREFILL_WAVES, 6) == hgqa.EINVAL
+    assert lib.hgqa_set_tuning(99, 0) == hgqa.EINVAL
+    assert "knob" in hgqa.hgqa_last_error()
+    for w in (4, 8, 0):
+        assert lib.hgqa_set_tuning(hgqa.TUNE_PREFILL_WAVES, w) == hgqa.OK
+
+
+def test_binding_checks_shapes_against_the_descriptor(lib):
+    """The binding takes Hq, Hkv = Hq / G and D from the layer descriptor, as
+    the kernels do, so a cache, key or query tensor of another head count or
+    head_dim is refused before anything is launched (CPU tensors: the shape
+    check comes before the device check)."""
+    import torch
+    L = hgqa.layer(0, 0, 16, 4, 128, 1e4)                 # Hq 16, Hkv 4, D 128
+    bf = torch.bfloat16
+    B, n, cap = 2, 3, 64
+    good = dict(q=torch.zeros(B, 16, 128, dtype=bf), g=torch.zeros(B, 16, dtype=bf),
+                kc=torch.zeros(B, 4, cap, 128, dtype=bf), lens=torch.ones(B, dtype=torch.int32))
+    bad_caches = [torch.zeros(B, 2, cap, 128, dtype=bf),   # too few KV heads
+                  torch.zeros(B, 4, cap, 64, dtype=bf)]    # smaller head_dim
+    for kc in bad_caches:
+        with pytest.raises(ValueError, match="shape"):
+            hgqa.attn_decode(L, good["q"], good["g"], kc, kc.clone(), good["lens"], 10)
+        with pytest.raises(ValueError, match="shape"):
+            hgqa.kv_append(L, good["lens"], 10, torch.zeros(B, n, 4, 128, dtype=bf),
+                           torch.zeros(B, n, 4, 128, dtype=bf), kc, kc.clone())
+        with pytest.raises(ValueError, match="shape"):
+            hgqa.attn_prefill_chunk(L, 5, torch.zeros(B, n, 16, 128, dtype=bf),
+                                    torch.zeros(B, n, 4, 128, dtype=bf),
+                                    torch.zeros(B, n, 4, 128, dtype=bf),
+                                    torch.zeros(B, n, 16, dtype=bf), kc, kc.clone())
+    # new keys with the cache's (wrong) head count are refused too
+    with pytest.raises(ValueError, match="shape"):
+        hgqa.kv_append(L, good["lens"], 10, torch.zeros(B, n, 2, 128, dtype=bf),
+                       torch.zeros(B, n, 2, 128, dtype=bf), bad_caches[0], bad_caches[0].clone())
+    with pytest.raises(ValueError, match="shape"):
+        hgqa.attn_prefill(L, torch.zeros(1, 5, 16, 64, dtype=bf), torch.zeros(1, 5, 4, 64, dtype=bf),
+                          torch.zeros(1, 5, 4, 64, dtype=bf), torch.zeros(1, 5, 16, dtype=bf))

@@ -1,7 +1,8 @@
 """Chunked prefill on the GPU against the fp64 oracle.
 
 A chunk of n tokens at positions p0..p0+n-1 continues a sequence whose first
-p0 positions sit in the layer's cache. Its output must equal the plain prefill
+p0 positions sit in the layer's cache; each sequence of a batch may have its
+own p0. Its output must equal the plain prefill
 definition of the whole sequence at the chunk's rows (the oracle evaluates
 exactly those rows), and afterwards the cache must hold what kv_append of the
 whole sequence leaves (bit-exact). Chunks with n = 4 are the multi-token
@@ -31,6 +32,15 @@ CASES = [
     (LayerShape(SLIDING, 64, 4, 1, 64, 1e4, 1.0), hgqa.FP32, 70, 40),
     (LayerShape(FULL, 0, 6, 2, 128, 5e6, 0.5), hgqa.FP32, 50, 20),
     (LayerShape(FULL, 0, 8, 1, 128, 1e4, 1.0, 0.0, (2.0, 1.0, 4.0, 256)), hgqa.BF16, 300, 100),
+    # every sequence at its own position: a 1 + 3 verify step over full caches
+    # and over rings, ragged chunks over a full cache with partial rotary, a
+    # ring with one sequence still inside its first window, and fp32
+    (LayerShape(FULL, 0, 64, 8, 128, 5e6, 0.5), hgqa.BF16, [1000, 3, 2500, 777], 4),
+    (LayerShape(SLIDING, 512, 96, 8, 128, 1e4, 1.0), hgqa.BF16, [1300, 20, 600], 4),
+    (LayerShape(FULL, 0, 16, 2, 128, 5e6, 0.5), hgqa.BF16, [0, 513, 64], 300),
+    (LayerShape(SLIDING, 64, 8, 2, 128, 1e4, 1.0), hgqa.BF16, [10, 200], 90),
+    (LayerShape(FULL, 0, 8, 1, 128, 0.0, 1.0), hgqa.BF16, [5, 4000], 2100),
+    (LayerShape(FULL, 0, 6, 2, 128, 5e6, 0.5), hgqa.FP32, [50, 0, 7], 20),
 ]
 B = 2
 
@@ -40,32 +50,40 @@ def _cap(shape, total):
 
 
 def _chunk_case(shape, dtype, p0, n, idx):
-    total = p0 + n
+    """p0: the start position of every sequence, or a list with one per sequence."""
+    starts = list(p0) if isinstance(p0, (list, tuple)) else [p0] * B
+    nb = len(starts)
+    total = max(starts) + n
     what = f"chunk[{idx}] {shape} p0 {p0} n {n}"
     print(what, flush=True)
-    q, k, v, g = prefill_inputs(shape, B, total, dtype, (0, 300 + idx, 0))
+    q, k, v, g = prefill_inputs(shape, nb, total, dtype, (0, 300 + idx, 0))
     L = hgqa.layer_from_shape(shape, dtype)
     cap = _cap(shape, total)
-    kc = torch.zeros(B, shape.num_kv_heads, cap, shape.head_dim, dtype=tdtype(dtype), device=DEV)
+    kc = torch.zeros(nb, shape.num_kv_heads, cap, shape.head_dim, dtype=tdtype(dtype), device=DEV)
     vc = torch.zeros_like(kc)
-    zeros = torch.zeros(B, dtype=torch.int32, device=DEV)
-    if p0 > 0:
-        hgqa.kv_append(L, zeros, p0, k[:, :p0].contiguous().to(DEV), v[:, :p0].contiguous().to(DEV),
-                       kc, vc)
-    out = hgqa.attn_prefill_chunk(L, p0, q[:, p0:].contiguous().to(DEV),
-                                  k[:, p0:].contiguous().to(DEV), v[:, p0:].contiguous().to(DEV),
-                                  g[:, p0:].contiguous().to(DEV), kc, vc)
-    # the cache the whole sequence leaves through kv_append
+    zero = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for b, s0 in enumerate(starts):
+        if s0 > 0:
+            hgqa.kv_append(L, zero, s0, k[b:b + 1, :s0].contiguous().to(DEV),
+                           v[b:b + 1, :s0].contiguous().to(DEV), kc[b:b + 1], vc[b:b + 1])
+    pick = lambda t: torch.stack([t[b, s0:s0 + n] for b, s0 in enumerate(starts)]).contiguous()
+    sp = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    out = hgqa.attn_prefill_chunk(L, sp, pick(q).to(DEV), pick(k).to(DEV), pick(v).to(DEV),
+                                  pick(g).to(DEV), kc, vc, max_end_pos=total)
+    # the cache each whole sequence leaves through kv_append
     kw = torch.zeros_like(kc)
     vw = torch.zeros_like(vc)
-    hgqa.kv_append(L, zeros, total, k.to(DEV), v.to(DEV), kw, vw)
+    for b, s0 in enumerate(starts):
+        hgqa.kv_append(L, zero, s0 + n, k[b:b + 1, :s0 + n].contiguous().to(DEV),
+                       v[b:b + 1, :s0 + n].contiguous().to(DEV), kw[b:b + 1], vw[b:b + 1])
     torch.cuda.synchronize()
     assert torch.equal(kc, kw) and torch.equal(vc, vw), f"{what}: cache differs from kv_append"
 
-    rows = [(b, t, h) for b in range(B) for t in range(p0, total) for h in range(shape.num_q_heads)]
+    rows = [(b, t, h) for b, s0 in enumerate(starts) for t in range(s0, s0 + n)
+            for h in range(shape.num_q_heads)]
     ref = oracle.prefill_rows(f64(q), f64(k), f64(v), f64(g), spec(shape), rows)
-    got = f64(out).reshape(B, n, shape.num_q_heads, shape.head_dim)
-    got = np.stack([got[b, t - p0, h] for (b, t, h) in rows])
+    got = f64(out).reshape(nb, n, shape.num_q_heads, shape.head_dim)
+    got = np.stack([got[b, t - starts[b], h] for (b, t, h) in rows])
     assert_close(got, ref, dtype, what)
 
 
@@ -78,14 +96,14 @@ def test_chunk_matches_whole_sequence_prefill(idx):
 
 # Both workgroup shapes of the bf16 kernel (4 and 8 waves) on chunks over a
 # ring and over a full cache, whatever the launcher would pick.
-WAVE_CASES = [1, 3, 6]
+WAVE_CASES = [1, 3, 6, 13, 15]
 
 
 @pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("idx", WAVE_CASES)
-def test_chunk_both_workgroup_shapes(idx, waves, monkeypatch):
+def test_chunk_both_workgroup_shapes(idx, waves, tuning):
     require_gpu()
-    monkeypatch.setenv("HGQA_PREFILL_WAVES", str(waves))
+    tuning(hgqa.TUNE_PREFILL_WAVES, waves)
     shape, dtype, p0, n = CASES[idx]
     _chunk_case(shape, dtype, p0, n, idx)
 

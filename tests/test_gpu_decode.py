@@ -230,7 +230,7 @@ def test_decode_is_deterministic():
 
 
 @pytest.mark.parametrize("split_keys", [None, 128, 1024, 1 << 20])
-def test_split_counts_agree(split_keys, monkeypatch):
+def test_split_counts_agree(split_keys, tuning):
     """The same decode with the keys cut into different split counts (the
     tuning override fixes the keys per split; 1 << 20 gives one split). Every
     plan matches the oracle. Against the one-split output the difference is
@@ -246,12 +246,9 @@ def test_split_counts_agree(split_keys, monkeypatch):
     g = synth.host_normal((4, 16), (0, 303, 0, synth.GATE)).to(DEV)
     L = hgqa.layer_from_shape(shape, hgqa.BF16)
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    monkeypatch.setenv("HGQA_DECODE_SPLIT_KEYS", str(1 << 20))
+    tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 1 << 20)
     one = hgqa.attn_decode(L, q, g, kc, vc, seq, max(lens))
-    if split_keys is None:
-        monkeypatch.delenv("HGQA_DECODE_SPLIT_KEYS")
-    else:
-        monkeypatch.setenv("HGQA_DECODE_SPLIT_KEYS", str(split_keys))
+    tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 0 if split_keys is None else split_keys)
     out = hgqa.attn_decode(L, q, g, kc, vc, seq, max(lens))
     torch.cuda.synchronize()
     ref = oracle.decode(f64(q), f64(g), okc, ovc, lens, spec(shape))

@@ -83,9 +83,9 @@ WAVE_CASES = [
 
 @pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("idx", range(len(WAVE_CASES)))
-def test_prefill_both_workgroup_shapes(idx, waves, monkeypatch):
+def test_prefill_both_workgroup_shapes(idx, waves, tuning):
     require_gpu()
-    monkeypatch.setenv("HGQA_PREFILL_WAVES", str(waves))
+    tuning(hgqa.TUNE_PREFILL_WAVES, waves)
     shape, B, T = WAVE_CASES[idx]
     q, k, v, g = prefill_inputs(shape, B, T, hgqa.BF16, (0, 170 + idx, 0))
     out = run_prefill(shape, hgqa.BF16, q, k, v, g)
