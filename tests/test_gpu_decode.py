@@ -287,32 +287,44 @@ def _c5_state(layer_index):
 
 @pytest.mark.parametrize("layer_index", [0, 1])
 def test_batched_decode_full_size(layer_index):
+    """The batched decode workload after its one-token append: every sequence
+    of the ring layer, and 16 sequences of the full layer (the shortest, the
+    longest and 14 seeded others). The append writes only slot L - 1 (or
+    (L - 1) mod W), so the oracle's cache is the GPU cache's other slots plus
+    the oracle's own append of the new token; one sequence at a time, so host
+    memory stays bounded."""
     require_gpu()
     shape, lens, kc, vc, k_new, v_new, q, g = _c5_state(layer_index)
     B = len(lens)
-    # oracle copies of the sequences it will check, before the new token lands
-    if shape.layer_type == SLIDING:
-        picks = list(range(B))
-    else:
-        order = np.argsort(lens)
-        picks = sorted({int(order[0]), int(order[-1]), 7, 40})
-    slices = {}
-    for b in picks:
-        n = int(lens[b]) if shape.layer_type == FULL else shape.window
-        slices[b] = (f64(kc[b:b + 1, :, :n]), f64(vc[b:b + 1, :, :n]))
     L = hgqa.layer_from_shape(shape, hgqa.BF16)
     start = torch.tensor(lens - 1, dtype=torch.int32, device=DEV)
     hgqa.kv_append(L, start, int(lens.max()), k_new.to(DEV), v_new.to(DEV), kc, vc)
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
     out = hgqa.attn_decode(L, q.to(DEV), g.to(DEV), kc, vc, seq, int(lens.max()))
     torch.cuda.synchronize()
+    if shape.layer_type == SLIDING:
+        picks = list(range(B))
+    else:
+        order = np.argsort(lens)
+        rng = np.random.default_rng(5)
+        others = [int(b) for b in rng.permutation(order[1:-1])[:14]]
+        picks = sorted({int(order[0]), int(order[-1])} | set(others))
+    assert len(picks) >= 16
     got, ref = [], []
     for b in picks:
-        okc, ovc = slices[b]
+        Lb = int(lens[b])
+        n = Lb if shape.layer_type == FULL else shape.window
+        slot = (Lb - 1) % n if shape.layer_type == SLIDING else Lb - 1
+        okc = f64(kc[b:b + 1, :, :n])
+        ovc = f64(vc[b:b + 1, :, :n])
+        okc[:, :, slot] = 0.0   # the oracle writes the new token itself
+        ovc[:, :, slot] = 0.0
         okc, ovc = oracle.kv_append(okc, ovc, f64(k_new[b:b + 1]), f64(v_new[b:b + 1]),
-                                    [int(lens[b]) - 1], spec(shape))
-        ref.append(oracle.decode(f64(q[b:b + 1]), f64(g[b:b + 1]), okc, ovc,
-                                 [int(lens[b])], spec(shape))[0])
+                                    [Lb - 1], spec(shape))
+        ref.append(oracle.decode(f64(q[b:b + 1]), f64(g[b:b + 1]), okc, ovc, [Lb],
+                                 spec(shape))[0])
         got.append(f64(out[b]))
+        del okc, ovc
     assert_close(np.stack(got), np.stack(ref), hgqa.BF16,
-                 f"batched decode layer {layer_index}: sequences {picks[:8]}...")
+                 f"batched decode layer {layer_index}: {len(picks)} sequences incl. lengths "
+                 f"{int(lens.min())} and {int(lens.max())}")

@@ -2,9 +2,11 @@
 
 Small shapes are compared on every output element (several 64-key tiles,
 ragged tails, every supported GQA ratio, both head dims, partial rotary,
-base 0, window 1 and window >= T). Full-size workloads are compared on
-sampled rows the oracle computes one by one: rows at the start, around the
-window edge, at the end, and seeded random rows.
+base 0, window 1 and window >= T). At full size, the Step sliding layer is
+compared on every element and each Muse sliding layer on every row of one KV
+head; the full layers, whose oracle costs tens of TFLOP, on sampled rows the
+oracle computes one by one: every head over the opening positions, around
+the window edge and at the end, and seeded random rows.
 """
 import numpy as np
 import pytest
@@ -135,45 +137,91 @@ class Rows:
         return f64(self.t[idx])
 
 
-def sample_rows(B, T, Hq, W, n_random, seed):
+def sample_rows(B, T, Hq, W, n_random, seed, band=0, heads=None):
+    """Rows (b, t, h) for a sampled comparison: every head at the first
+    `band` positions, at the window edge and at the end, plus seeded random
+    rows; heads restricts the heads."""
     rng = np.random.default_rng(seed)
-    edge = {0, 1, 2, T - 2, T - 1}
+    hs = list(range(Hq)) if heads is None else list(heads)
+    edge = set(range(min(band, T))) | {0, 1, 2, T - 2, T - 1}
     if W:
         edge |= {W - 2, W - 1, W, W + 1, 2 * W + 3}
     edge = sorted(t for t in edge if 0 <= t < T)
-    rows = [(b, t, h) for b in range(B) for t in edge for h in range(Hq)]
+    rows = [(b, t, h) for b in range(B) for t in edge for h in hs]
     for _ in range(n_random):
-        rows.append((int(rng.integers(B)), int(rng.integers(T)), int(rng.integers(Hq))))
+        rows.append((int(rng.integers(B)), int(rng.integers(T)), hs[int(rng.integers(len(hs)))]))
     return rows
 
 
-def check_sampled(shape, wl, li, n_random=600):
-    q, k, v, g = prefill_inputs(shape, wl.batch, wl.seq_len, hgqa.BF16, (0, wl.wid, li))
-    out = run_prefill(shape, hgqa.BF16, q, k, v, g)
-    rows = sample_rows(wl.batch, wl.seq_len, shape.num_q_heads, shape.window, n_random, li)
+def check_rows(out, inputs, shape, rows, what):
+    q, k, v, g = inputs
     ref = oracle.prefill_rows(Rows(q), Rows(k), Rows(v), Rows(g), spec(shape), rows)
     idx = torch.tensor(rows)
     got = out[idx[:, 0], idx[:, 1], idx[:, 2]]
-    return assert_close(got, ref, hgqa.BF16, f"{wl.name} layer {li}: {len(rows)} sampled rows")
+    return assert_close(got, ref, hgqa.BF16, f"{what}: {len(rows)} sampled rows")
+
+
+def full_size_run(wl, li):
+    shape = wl.layers[li]
+    inputs = prefill_inputs(shape, wl.batch, wl.seq_len, hgqa.BF16, (0, wl.wid, li))
+    return shape, inputs, run_prefill(shape, hgqa.BF16, *inputs)
 
 
 def test_step_sliding_layer_full_size():
+    """Every element of the Step sliding layer (T 8192, 96 Q / 8 KV heads,
+    window 512) against the oracle."""
     require_gpu()
     wl = workloads.STEP_SLIDING
-    check_sampled(wl.layers[0], wl, 0)
+    shape, (q, k, v, g), out = full_size_run(wl, 0)
+    ref = oracle.prefill(f64(q), f64(k), f64(v), f64(g), spec(shape))
+    assert_close(out, ref, hgqa.BF16, f"{wl.name}: every element")
 
 
 def test_step_full_layer_full_size():
+    """The Step full layer (T 32768): every head at the first 64 positions,
+    at the end, and 1500 seeded random rows."""
     require_gpu()
     wl = workloads.STEP_FULL
-    check_sampled(wl.layers[0], wl, 0, n_random=300)
+    shape, inputs, out = full_size_run(wl, 0)
+    rows = sample_rows(wl.batch, wl.seq_len, shape.num_q_heads, 0, 1500, 0, band=64)
+    check_rows(out, inputs, shape, rows, wl.name)
 
 
-def test_muse_block_full_size():
+@pytest.mark.parametrize("li", [0, 1, 2])
+def test_muse_sliding_layer_full_size(li):
+    """A sliding layer of the Muse block (T 65536, window 2048, 16 Q heads per
+    KV head): every row of one KV head's 16 query heads against the oracle's
+    prefill of that head group, and sampled rows of the other KV head (the
+    first 2048 positions of every head among them)."""
     require_gpu()
     wl = workloads.MUSE_BLOCK
-    for li, shape in enumerate(wl.layers):
-        check_sampled(shape, wl, li, n_random=200)
+    shape, (q, k, v, g), out = full_size_run(wl, li)
+    G = shape.gqa_ratio
+    kv = li % 2
+    hs = slice(kv * G, (kv + 1) * G)
+    one = oracle.LayerSpec(oracle.SLIDING, shape.window, G, 1, shape.head_dim, shape.rope_theta,
+                           shape.rotary_fraction)
+    ref = oracle.prefill(f64(q[:, :, hs]), f64(k[:, :, kv:kv + 1]), f64(v[:, :, kv:kv + 1]),
+                         f64(g[:, :, hs]), one)
+    assert_close(out[:, :, hs], ref, hgqa.BF16,
+                 f"{wl.name} layer {li}: every row of KV head {kv}")
+    del ref
+    other = range((1 - kv) * G, (2 - kv) * G)
+    rows = sample_rows(wl.batch, wl.seq_len, shape.num_q_heads, shape.window, 400, li,
+                       band=shape.window, heads=[(1 - kv) * G])
+    rows += sample_rows(wl.batch, wl.seq_len, shape.num_q_heads, shape.window, 400, 10 + li,
+                        heads=other)
+    check_rows(out, (q, k, v, g), shape, rows, f"{wl.name} layer {li}, KV head {1 - kv}")
+
+
+def test_muse_full_layer_full_size():
+    """The Muse block's full layer (T 65536, base 0): every head at the first
+    128 positions, at the end, and 1000 seeded random rows."""
+    require_gpu()
+    wl = workloads.MUSE_BLOCK
+    shape, inputs, out = full_size_run(wl, 3)
+    rows = sample_rows(wl.batch, wl.seq_len, shape.num_q_heads, 0, 1000, 3, band=128)
+    check_rows(out, inputs, shape, rows, f"{wl.name} layer 3")
 
 
 def test_prefill_is_deterministic():

@@ -251,11 +251,22 @@ def test_matches_sdpa_without_rotation(lt, W):
 
 # ------------------------------------------------------- decode and cache
 
-@pytest.mark.parametrize("lt,W,f,theta", [(FULL, 0, 0.5, 5e6), (SLIDING, 8, 1.0, 1e4),
-                                          (SLIDING, 64, 1.0, 1e4)])
-def test_decode_equals_last_prefill_row(lt, W, f, theta):
+# llama3 scaling with a short original context (16 positions), so that on a
+# 16-dim head with r = 8 the first pair is blended and the others divided by
+# the factor (wavelengths 6.3, 298, 1.4e4, 6.6e5 against 16/4 and 16/1)
+SCALED = (2.0, 1.0, 4.0, 16)
+
+
+@pytest.mark.parametrize("lt,W,f,theta,sc", [(FULL, 0, 0.5, 5e6, None), (SLIDING, 8, 1.0, 1e4, None),
+                                             (SLIDING, 64, 1.0, 1e4, None),
+                                             (FULL, 0, 0.5, 5e6, SCALED),
+                                             (FULL, 0, 1.0, 1e4, (3.0, 1.0, 8.0, 64))])
+def test_decode_equals_last_prefill_row(lt, W, f, theta, sc):
+    """Decode over a cache that kv_append filled equals the last prefill row:
+    with frequency scaling the cache's keys, the decode query and prefill's
+    queries and keys must all use the same rescaled frequencies."""
     B, L, Hq, Hkv, D = 2, 29, 4, 2, 16
-    layer = LayerSpec(lt, W, Hq, Hkv, D, theta, f)
+    layer = LayerSpec(lt, W, Hq, Hkv, D, theta, f, rope_scaling=sc)
     q, k, v, g = _inputs(B, L, Hq, Hkv, D, 31)
     cap = W if lt == SLIDING else 40
     kc = np.zeros((B, Hkv, cap, D))
@@ -279,6 +290,34 @@ def test_decode_with_appends_in_pieces():
         kc, vc = oracle.kv_append(kc, vc, k[:, p:p + 1], v[:, p:p + 1], np.array([p]), layer)
         yd = oracle.decode(q[:, p], g[:, p], kc, vc, np.array([p + 1]), layer)
         np.testing.assert_allclose(yd, yp[:, p], rtol=0, atol=1e-12)
+
+
+def test_scaled_full_layer_decode_with_appends_in_pieces():
+    """A full layer with llama3 scaling, appended in uneven pieces (positions
+    past the original context included) and decoded at each piece's end,
+    reproduces the prefill rows; the scaling changes those rows."""
+    B, T, Hq, Hkv, D = 1, 40, 4, 1, 16
+    layer = LayerSpec(FULL, 0, Hq, Hkv, D, 5e6, 0.5, rope_scaling=SCALED)
+    plain = LayerSpec(FULL, 0, Hq, Hkv, D, 5e6, 0.5)
+    q, k, v, g = _inputs(B, T, Hq, Hkv, D, 43)
+    yp = oracle.prefill(q, k, v, g, layer)
+    assert np.abs(yp - oracle.prefill(q, k, v, g, plain)).max() > 1e-3
+    kc = np.zeros((B, Hkv, T, D))
+    vc = np.zeros((B, Hkv, T, D))
+    cuts = [0, 1, 7, 8, 20, 33, 40]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        kc, vc = oracle.kv_append(kc, vc, k[:, a:b], v[:, a:b], np.array([a]), layer)
+        yd = oracle.decode(q[:, b - 1], g[:, b - 1], kc, vc, np.array([b]), layer)
+        np.testing.assert_allclose(yd, yp[:, b - 1], rtol=0, atol=1e-12)
+    # the cache holds keys rotated at their positions with the rescaled frequencies
+    om = oracle.llama3_frequencies(np.power(5e6, -2.0 * np.arange(4) / 8), *SCALED)
+    p = 37
+    ang = p * om
+    x = k[0, p, 0]
+    want = x.copy()
+    want[:4] = x[:4] * np.cos(ang) - x[4:8] * np.sin(ang)
+    want[4:8] = x[4:8] * np.cos(ang) + x[:4] * np.sin(ang)
+    np.testing.assert_allclose(kc[0, 0, p], want, rtol=0, atol=1e-14)
 
 
 def test_ring_at_least_as_long_as_history_equals_full_cache():
