@@ -23,7 +23,7 @@ TUNE_PREFILL_WAVES, TUNE_DECODE_SPLIT_KEYS = 1, 2
 
 EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "attn_prefill_chunk_workspace_bytes",
             "attn_prefill_chunk", "kv_append", "attn_decode_workspace_bytes", "attn_decode",
-            "hgqa_set_tuning", "hgqa_last_error")
+            "attn_decode_noalloc", "hgqa_set_tuning", "hgqa_last_error")
 
 
 class HgqaLayer(ctypes.Structure):
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_decode_workspace_bytes.restype = S
     lib.attn_decode.argtypes = [LP, I, P, P, P, P, I, P, I, P, S, P, P]
     lib.attn_decode.restype = ctypes.c_int
+    lib.attn_decode_noalloc.argtypes = [LP, I, P, P, P, P, I, P, I, P, P]
+    lib.attn_decode_noalloc.restype = ctypes.c_int
     lib.hgqa_set_tuning.argtypes = [I, I]
     lib.hgqa_set_tuning.restype = ctypes.c_int
     lib.hgqa_last_error.argtypes = []
@@ -265,4 +267,25 @@ def attn_decode(L: HgqaLayer, q, gate, k_cache, v_cache, seq_lens, max_seq_len: 
     _check(lib.attn_decode(ctypes.byref(L), B, _ptr(q), _ptr(gate), _ptr(k_cache),
                            _ptr(v_cache), cap, _ptr(seq_lens), int(max_seq_len),
                            _ptr(workspace), _nbytes(workspace), _ptr(out), _stream()))
+    return out
+
+
+def attn_decode_noalloc(L: HgqaLayer, q, gate, k_cache, v_cache, seq_lens, max_seq_len: int, out):
+    """attn_decode with the split partials in the library's static scratch: the
+    library allocates nothing and neither does this wrapper (out is the caller's)."""
+    lib = load_library()
+    Hq, Hkv, D = _heads(L)
+    B = q.shape[0]
+    cap = k_cache.shape[2]
+    dt = _torch_dtype(L)
+    _need(q, "q", (B, Hq, D), dt)
+    _need(gate, "gate", (B, Hq), dt)
+    _need(k_cache, "k_cache", (B, Hkv, cap, D), dt)
+    _need(v_cache, "v_cache", (B, Hkv, cap, D), dt)
+    _need(seq_lens, "seq_lens", (B,), torch.int32)
+    _need(out, "out", (B, Hq, D), dt)
+    _on_gpu(q=q, gate=gate, k_cache=k_cache, v_cache=v_cache, seq_lens=seq_lens, out=out)
+    _check(lib.attn_decode_noalloc(ctypes.byref(L), B, _ptr(q), _ptr(gate), _ptr(k_cache),
+                                   _ptr(v_cache), cap, _ptr(seq_lens), int(max_seq_len), _ptr(out),
+                                   _stream()))
     return out

@@ -247,6 +247,23 @@ int attn_decode(const hgqa_layer* layer, int32_t batch, const void* q,
                 void* out, void* stream);
 
 /*
+ * attn_decode for callers that cannot allocate: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc. The same
+ * arguments without the workspace; the per-split partials go to a static
+ * device array of the library (16 MiB, one copy per GPU, held until the
+ * process ends), whose address on each GPU is looked up on that GPU's first
+ * call. Nothing is allocated. A plan that needs more than 16 MiB of partials
+ * (attn_decode_workspace_bytes above it) returns HGQA_ENOSPACE before
+ * anything is enqueued. Calls on one GPU share the array: calls that overlap
+ * on one GPU (other streams, other threads) race, and the caller must order
+ * them. The output equals attn_decode's for the same inputs.
+ */
+int attn_decode_noalloc(const hgqa_layer* layer, int32_t batch, const void* q,
+                        const void* gate, const void* k_cache, const void* v_cache,
+                        int32_t cache_capacity, const int32_t* seq_lens,
+                        int32_t max_seq_len, void* out, void* stream);
+
+/*
  * Tuning overrides, for tests and measurements only: process-wide settings
  * that later calls read when they plan their launches. value 0 restores the
  * library's own choice.
