@@ -434,17 +434,28 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     const uint16_t* ks = sm.st[st].k;
     const uint16_t* vs = sm.st[st].v;
 
-    // S^T for two 32-key blocks
+    // S^T for two 32-key blocks, the blocks' products alternating; each K
+    // fragment read runs RA products ahead of its product, so the LDS
+    // latency hides behind the products in between
     f32x16_t S[2];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      S[kb] = FIRST ? f32x16_t{} : negm;
-      const int key = 32 * kb + n;
+    for (int kb = 0; kb < NKB; ++kb) S[kb] = FIRST ? f32x16_t{} : negm;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int key = 32 * kb + n;
         const int pos = (2 * s + g) ^ Swz<D>::k(key);
         bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(ks + key * D + 8 * pos);
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], S[kb], 0, 0, 0);
+      }
+    {
+      constexpr int NM = NS * NKB, RA = 4 < NM ? 4 : NM;
+      __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);  // the first RA fragment reads
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
+        if (i + RA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read RA ahead
       }
     }
 
