@@ -555,7 +555,7 @@ def bench_verify(args, torch, hgqa, synth, acc, L, cache, key, lens_np):
     sp = torch.tensor(starts, dtype=torch.int32, device=dev)
     end = int(lens_np.max())
     out = torch.empty_like(q)
-    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, B, n), dtype=torch.uint8,
+    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, B, n, end), dtype=torch.uint8,
                      device=dev)
     fn = lambda: hgqa.attn_prefill_chunk(L, sp, q, kn, vn, g, kc, vc, max_end_pos=end, out=out,
                                          workspace=ws)
@@ -590,7 +590,7 @@ def bench_chunk(args, torch, hgqa, synth, workloads, acc):
     v = synth.host_normal((1, n, Hkv, D), key + (synth.V,)).to(dev)
     g = synth.host_normal((1, n, Hq), key + (synth.GATE,)).to(dev)
     out = torch.empty_like(q)
-    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, 1, n), dtype=torch.uint8,
+    ws = torch.empty(hgqa.attn_prefill_chunk_workspace_bytes(L, 1, n, p0 + n), dtype=torch.uint8,
                      device=dev)
     fn = lambda: hgqa.attn_prefill_chunk(L, p0, q, k, v, g, kc, vc, out=out, workspace=ws)
     for _ in range(args.warmup):

@@ -19,6 +19,7 @@ thread_local std::string g_last_error;
 // hgqa_set_tuning overrides (0: the library's own choice).
 std::atomic<int> g_prefill_waves{0};
 std::atomic<int> g_decode_split_keys{0};
+std::atomic<int> g_chunk_split_tiles{0};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -139,6 +140,16 @@ size_t chunk_ws(const Layer& l, int B, int T) {
   return rotated_k_bytes(l, B, T) + round256((size_t)B * T * l.half * sizeof(float2));
 }
 
+// The key-split plan of a chunk call (the same for the workspace query and
+// the call): fills a's split fields, returns the partial bytes (256-rounded).
+size_t plan_splits(const Layer& l, hgqa::PrefillArgs& a, int max_end_pos) {
+  a.k_cache = reinterpret_cast<const void*>(16);  // a chunk: the plan only tests for a cache
+  a.sliding = l.sliding;
+  a.window = l.window;
+  return round256(hgqa::plan_prefill_splits(a, l.elem, max_end_pos,
+                                            g_chunk_split_tiles.load(std::memory_order_relaxed)));
+}
+
 // Checks shared by the prefill entry points; n = tokens in this call, need =
 // the workspace bytes the call needs.
 int check_prefill_call(const Layer& l, int batch, int n, const void* q, const void* k,
@@ -175,6 +186,9 @@ hgqa::PrefillArgs prefill_args(const Layer& l, int batch, int n, const void* q, 
   a.start_pos = nullptr;
   a.max_end_pos = n;
   a.waves = g_prefill_waves.load(std::memory_order_relaxed);
+  a.num_splits = 1;
+  a.split_tiles = 0;
+  a.partial = nullptr;
   a.B = batch;
   a.T = n;
   a.Hq = l.Hq;
@@ -186,6 +200,19 @@ hgqa::PrefillArgs prefill_args(const Layer& l, int batch, int n, const void* q, 
   a.scale = l.scale;
   fill_rope(l, &a.rope);
   return a;
+}
+
+// Partial bytes of a chunk call's key splits (0 without splits).
+size_t split_ws(const Layer& l, int B, int n, int max_end_pos) {
+  hgqa::PrefillArgs a{};
+  a.B = B;
+  a.T = n;
+  a.Hq = l.Hq;
+  a.Hkv = l.Hkv;
+  a.G = l.G;
+  a.D = l.D;
+  a.waves = g_prefill_waves.load(std::memory_order_relaxed);
+  return plan_splits(l, a, max_end_pos);
 }
 
 }  // namespace
@@ -295,10 +322,11 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
   return ok();
 }
 
-size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t n_new) {
+size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch, int32_t n_new,
+                                          int32_t max_end_pos) {
   Layer l;
-  if (check_layer(layer, &l) != HGQA_OK || batch < 0 || n_new < 0) return 0;
-  return chunk_ws(l, batch, n_new);
+  if (check_layer(layer, &l) != HGQA_OK || batch < 0 || n_new < 0 || max_end_pos < n_new) return 0;
+  return chunk_ws(l, batch, n_new) + split_ws(l, batch, n_new, max_end_pos);
 }
 
 int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
@@ -320,7 +348,7 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
                 cache_capacity);
   if (batch == 0 || n_new == 0) return ok();
   rc = check_prefill_call(l, batch, n_new, q, k, v, gate, out, workspace, workspace_bytes,
-                          chunk_ws(l, batch, n_new));
+                          chunk_ws(l, batch, n_new) + split_ws(l, batch, n_new, max_end_pos));
   if (rc != HGQA_OK) return rc;
   if ((long long)batch * l.Hkv * cache_capacity * l.D > kMaxElems)
     return fail(HGQA_EUNSUPPORTED, "cache too large");
@@ -336,6 +364,8 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
 
   // Attention first: a ring still holds the W - 1 positions before the chunk.
   hgqa::PrefillArgs a = prefill_args(l, batch, n_new, q, k, v, gate, out, workspace);
+  if (plan_splits(l, a, max_end_pos) > 0)
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + chunk_ws(l, batch, n_new));
   a.start_pos = start_pos;
   a.max_end_pos = max_end_pos;
   a.cs_bstride = (size_t)n_new * l.half;
@@ -435,6 +465,10 @@ int hgqa_set_tuning(int32_t knob, int32_t value) {
     case HGQA_TUNE_DECODE_SPLIT_KEYS:
       if (value < 0) return fail(HGQA_EINVAL, "HGQA_TUNE_DECODE_SPLIT_KEYS must be >= 0");
       g_decode_split_keys.store(value, std::memory_order_relaxed);
+      return ok();
+    case HGQA_TUNE_CHUNK_SPLIT_TILES:
+      if (value < 0) return fail(HGQA_EINVAL, "HGQA_TUNE_CHUNK_SPLIT_TILES must be >= 0");
+      g_chunk_split_tiles.store(value, std::memory_order_relaxed);
       return ok();
     default:
       return fail(HGQA_EINVAL, "unknown tuning knob %d", knob);

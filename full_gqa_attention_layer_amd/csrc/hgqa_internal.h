@@ -47,7 +47,18 @@ struct PrefillArgs {
   const void* v_cache;
   int cap, ring;
   int waves;            // bf16 workgroup shape override: 0 automatic, 4 or 8
+  // Split over keys (chunks only): each row block's key tiles are cut into
+  // num_splits runs of split_tiles; each run writes per-row partials
+  // [B, T, Hq, num_splits, D + 4] fp32 (unnormalised output, log2-unit
+  // reference, sum) that a merge kernel combines. num_splits 1: no split.
+  int num_splits, split_tiles;
+  float* partial;
 };
+
+// Split plan of a chunk call whose longest sequence ends at max_end_pos
+// (split_tiles_override > 0 fixes the tiles per split; tuning only): sets
+// a.num_splits and a.split_tiles; returns the partial bytes it needs.
+size_t plan_prefill_splits(PrefillArgs& a, Elem e, int max_end_pos, int split_tiles_override);
 
 // Start position of sequence b in a prefill call (device side).
 __device__ __forceinline__ int prefill_p0(const PrefillArgs& a, int b) {

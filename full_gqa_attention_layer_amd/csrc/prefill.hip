@@ -24,6 +24,7 @@
 // tiles that cross the diagonal or the window edge are masked elementwise.
 #include "device_util.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace hgqa {
@@ -164,7 +165,9 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const int kvh = id % Hkv;
   const int rest = id / Hkv;
   const int b = rest % a.B;
-  const int rb = nrb - 1 - rest / a.B;
+  const int rest2 = rest / a.B;
+  const int split = kCache ? rest2 % a.num_splits : 0;  // key split (chunks only)
+  const int rb = nrb - 1 - (kCache ? rest2 / a.num_splits : rest2);
 
   // Rows of the block split into (position, head in group). R0 = t0 G + hg0
   // once; a local row r then needs only the small quotient (hg0 + r) / G,
@@ -189,6 +192,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
 
   const int rl = wave * kRowsPerWave + n;
   const bool row_ok = rl < nrows;
+  const bool wave_rows = wave * kRowsPerWave < nrows;  // uniform per wave
   int dt_row, hg_row;
   split_local(min(rl, nrows - 1), dt_row, hg_row);
   const int t_row = t0 + dt_row;
@@ -210,9 +214,25 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const size_t blk_row = (size_t)(b * T + t0) * Hq + kvh * G;
 
   // ---- key range of the workgroup (absolute positions)
-  const int j_lo = SL ? max(0, p0 + t_lo - a.window + 1) : 0;
-  const int ntiles = (p0 + t_hi + 1 - j_lo + kBN - 1) / kBN;
+  int j_lo = SL ? max(0, p0 + t_lo - a.window + 1) : 0;
+  int ntiles = (p0 + t_hi + 1 - j_lo + kBN - 1) / kBN;
   const int j_last = p0 + T - 1;
+
+  // A split takes tiles [split * split_tiles, ...) of the block's range and
+  // writes partials; a split past the range marks its rows empty.
+  const size_t prow = kCache ? ((size_t)(b * T + t_row) * Hq + kvh * G + hg_row) : 0;
+  float* const part = kCache ? a.partial + (prow * a.num_splits + split) * (D + 4) : nullptr;
+  if constexpr (kCache) {
+    if (a.num_splits > 1) {
+      const int first = split * a.split_tiles;
+      if (first >= ntiles) {
+        if (row_ok && g == 0) part[D] = -INFINITY;
+        return;
+      }
+      j_lo += first * kBN;
+      ntiles = min(ntiles - first, a.split_tiles);
+    }
+  }
 
   const uint16_t* kbase = kr + (size_t)(b * Hkv + kvh) * T * D;
   const uint16_t* vbase = vp + ((size_t)b * T * Hkv + kvh) * D;
@@ -431,6 +451,13 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     const int st = it & 1;
     const int j0 = j_lo + it * kBN;
     if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
+    if (kCache && !wave_rows) {
+      // a chunk of a few tokens leaves whole waves without rows: they only
+      // copy their share of the tiles (no products, no LDS fragment reads)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      return;
+    }
     const uint16_t* ks = sm.st[st].k;
     const uint16_t* vs = sm.st[st].v;
 
@@ -553,11 +580,28 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   if (j_lo + (ntiles - 1) * kBN + 32 > tw_hi) tile(ntiles - 1, Half{}, Later{});
   else tile(ntiles - 1, Full{}, Later{});
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if constexpr (kCache) {
+    if (a.num_splits > 1) {
+      // partial of this split: the unnormalised output and the sum relative
+      // to the reference (log2 units), which is -inf when the row saw no key
+      if (row_ok) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(part + 32 * db + 8 * q4 + 4 * g) =
+                f32x4_t{O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2], O[db][4 * q4 + 3]};
+        if (g == 0) *reinterpret_cast<float2*>(part + D) = make_float2(m_run, l_tot);
+      }
+      return;
+    }
+  }
+
   // ---- epilogue: normalise and gate in registers, then turn the O^T
   // fragments into row-major rows in LDS (stage 0, idle because the loop
   // ended on a barrier with no load in flight, or with 8 waves the Q/output
   // area) so that the stores write whole rows.
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = row_ok ? sigmoidf_dev(gate_logit) / l_tot : 0.0f;
   uint16_t* ow = (KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[0])) + wave * (kRowsPerWave * D);  // this wave's rows
 #pragma unroll
@@ -659,6 +703,27 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   if (lane + 64 < D) o[lane + 64] = o1 * f;
 }
 
+// Log-sum-exp merge of a chunk's key splits, then the gate: one block of D
+// threads per (sequence, row, head). Splits whose rows saw no key (reference
+// -inf) carry no weight.
+__global__ void prefill_merge_kernel(PrefillArgs a) {
+  const size_t row = blockIdx.x;  // (b T + t) Hq + h
+  const int D = a.D, d = threadIdx.x, ns = a.num_splits;
+  const float* pr = a.partial + row * ns * (D + 4);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (D + 4) + D]);
+  float acc = 0.0f, l = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float m = pr[s * (D + 4) + D];
+    if (m == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(m - M);
+    acc = fmaf(pr[s * (D + 4) + d], f, acc);
+    l = fmaf(pr[s * (D + 4) + D + 1], f, l);
+  }
+  const float gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[row]);
+  static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(sigmoidf_dev(gv) * acc / l);
+}
+
 // Waves per workgroup. 8 (one workgroup per CU, each K/V tile copied once
 // for 256 rows) when a block visits many tiles: full layers and windows of
 // 1024 keys or more (measured: full layers 4-5% faster, W = 2048 3-4%). 4
@@ -682,6 +747,41 @@ static void launch_bf16(const PrefillArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, kCache, KW, false>), grid, dim3(KW * 64), 0, s, a);
 }
 
+// Chunk calls whose grid would not fill the chip twice over (few rows, few
+// sequences) split each block's key range, at least kMinSplitTiles tiles per
+// split, aiming at kSplitTargetBlocks workgroups; bf16 only.
+constexpr int kMinSplitTiles = 16;
+constexpr int kSplitTargetBlocks = 2048;
+
+size_t plan_prefill_splits(PrefillArgs& a, Elem e, int max_end_pos, int split_tiles_override) {
+  a.num_splits = 1;
+  a.split_tiles = 0;
+  if (e != Elem::BF16 || a.k_cache == nullptr || a.B == 0 || a.T == 0) return 0;
+  const int kw = prefill_waves(a);
+  const long long nrb = ((long long)a.T * a.G + kw * kRowsPerWave - 1) / (kw * kRowsPerWave);
+  const long long blocks = nrb * a.B * a.Hkv;
+  // longest key range of a block: the whole context (full) or the window
+  // plus the block's positions (sliding)
+  const long long span = a.sliding ? std::min<long long>(max_end_pos, (long long)a.window + a.T)
+                                   : max_end_pos;
+  const long long tiles = span / kBN + 2;
+  long long st;
+  if (split_tiles_override > 0) {
+    st = split_tiles_override;
+  } else {
+    if (blocks * kw >= 2LL * 256 * 8) return 0;
+    long long ns = (kSplitTargetBlocks + blocks - 1) / blocks;
+    ns = std::min(ns, tiles / kMinSplitTiles);
+    if (ns <= 1) return 0;
+    st = (tiles + ns - 1) / ns;
+  }
+  const long long ns = (tiles + st - 1) / st;
+  if (ns <= 1) return 0;
+  a.num_splits = (int)ns;
+  a.split_tiles = (int)st;
+  return (size_t)a.B * a.T * a.Hq * ns * (a.D + 4) * sizeof(float);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   hipError_t err = launch_prefill_prepass(a, e, s);
   if (err != hipSuccess) return err;
@@ -694,7 +794,7 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const bool cache = a.k_cache != nullptr;
   const int kw = prefill_waves(a);
   const long long rows = (long long)kw * kRowsPerWave;
-  const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv;
+  const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv * (cache ? a.num_splits : 1);
   const dim3 grid((unsigned)blocks);
   if (a.D == 128) {
     if (cache && kw == 8) launch_bf16<128, true, 8>(a, grid, s);
@@ -705,6 +805,10 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
     if (cache) launch_bf16<64, true, 4>(a, grid, s);
     else launch_bf16<64, false, 4>(a, grid, s);
   }
+  err = hipGetLastError();
+  if (err != hipSuccess || !cache || a.num_splits <= 1) return err;
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)((long long)a.B * a.T * a.Hq)), dim3(a.D), 0,
+                     s, a);
   return hipGetLastError();
 }
 

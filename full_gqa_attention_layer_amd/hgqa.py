@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhgqa.so"
 FULL, SLIDING = 0, 1
 BF16, FP32 = 0, 1
 OK, EINVAL, EUNSUPPORTED, ENOSPACE, EHIP = 0, -1, -2, -3, -4
-TUNE_PREFILL_WAVES, TUNE_DECODE_SPLIT_KEYS = 1, 2
+TUNE_PREFILL_WAVES, TUNE_DECODE_SPLIT_KEYS, TUNE_CHUNK_SPLIT_TILES = 1, 2, 3
 
 EXPORTED = ("attn_prefill_workspace_bytes", "attn_prefill", "attn_prefill_chunk_workspace_bytes",
             "attn_prefill_chunk", "kv_append", "attn_decode_workspace_bytes", "attn_decode",
@@ -61,7 +61,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_prefill_workspace_bytes.restype = S
     lib.attn_prefill.argtypes = [LP, I, I, P, P, P, P, P, P, S, P]
     lib.attn_prefill.restype = ctypes.c_int
-    lib.attn_prefill_chunk_workspace_bytes.argtypes = [LP, I, I]
+    lib.attn_prefill_chunk_workspace_bytes.argtypes = [LP, I, I, I]
     lib.attn_prefill_chunk_workspace_bytes.restype = S
     lib.attn_prefill_chunk.argtypes = [LP, I, I, P, I, P, P, P, P, P, P, I, P, P, S, P]
     lib.attn_prefill_chunk.restype = ctypes.c_int
@@ -180,8 +180,10 @@ def attn_prefill(L: HgqaLayer, q, k, v, gate, out=None, workspace=None):
     return out
 
 
-def attn_prefill_chunk_workspace_bytes(L: HgqaLayer, batch: int, n_new: int) -> int:
-    return int(load_library().attn_prefill_chunk_workspace_bytes(ctypes.byref(L), batch, n_new))
+def attn_prefill_chunk_workspace_bytes(L: HgqaLayer, batch: int, n_new: int,
+                                       max_end_pos: int) -> int:
+    return int(load_library().attn_prefill_chunk_workspace_bytes(ctypes.byref(L), batch, n_new,
+                                                                 max_end_pos))
 
 
 def attn_prefill_chunk(L: HgqaLayer, start_pos, q, k, v, gate, k_cache, v_cache,
@@ -212,7 +214,7 @@ def attn_prefill_chunk(L: HgqaLayer, start_pos, q, k, v, gate, k_cache, v_cache,
     _need(out, "out", (B, n, Hq, D), dt)
     _on_gpu(start_pos=start_pos, q=q, k=k, v=v, gate=gate, k_cache=k_cache, v_cache=v_cache,
             out=out, workspace=workspace)
-    need = attn_prefill_chunk_workspace_bytes(L, B, n)
+    need = attn_prefill_chunk_workspace_bytes(L, B, n, int(max_end_pos))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.attn_prefill_chunk(ctypes.byref(L), B, n, _ptr(start_pos), int(max_end_pos),

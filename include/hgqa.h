@@ -141,14 +141,16 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len,
                  void* stream);
 
 /*
- * Scratch bytes attn_prefill_chunk needs: the rotated new keys
- * [B, Hkv, n_new, D] in the layer dtype and one cos/sin table per sequence
- * [B, n_new, r/2] of float pairs (the sequences start at different
- * positions), each part rounded up to 256 bytes. Returns 0 for an invalid
- * layer.
+ * Scratch bytes attn_prefill_chunk needs for a call whose sequences end at
+ * most at max_end_pos: the rotated new keys [B, Hkv, n_new, D] in the layer
+ * dtype, one cos/sin table per sequence [B, n_new, r/2] of float pairs (the
+ * sequences start at different positions), and, when the call is split over
+ * keys (few rows over long caches: a multi-token step), per-split partial
+ * results [B, n_new, Hq, splits, D + 4] float32; each part rounded up to 256
+ * bytes. Returns 0 for an invalid layer or max_end_pos < n_new.
  */
 size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch,
-                                          int32_t n_new);
+                                          int32_t n_new, int32_t max_end_pos);
 
 /*
  * Chunked prefill: the n_new new tokens of sequence b, at absolute positions
@@ -270,10 +272,13 @@ int attn_decode_noalloc(const hgqa_layer* layer, int32_t batch, const void* q,
  *   HGQA_TUNE_PREFILL_WAVES      4 or 8 waves per bf16 prefill workgroup
  *                                (head_dim 128 only; other layers ignore it)
  *   HGQA_TUNE_DECODE_SPLIT_KEYS  keys per decode split (rounded up to 32)
+ *   HGQA_TUNE_CHUNK_SPLIT_TILES  64-key tiles per key split of a bf16
+ *                                attn_prefill_chunk (a value at or above the
+ *                                longest key range means no split)
  * Returns HGQA_EINVAL for an unknown knob or value. Changing a knob while
  * another thread is inside a call gives that call either setting.
  */
-enum { HGQA_TUNE_PREFILL_WAVES = 1, HGQA_TUNE_DECODE_SPLIT_KEYS = 2 };
+enum { HGQA_TUNE_PREFILL_WAVES = 1, HGQA_TUNE_DECODE_SPLIT_KEYS = 2, HGQA_TUNE_CHUNK_SPLIT_TILES = 3 };
 int hgqa_set_tuning(int32_t knob, int32_t value);
 
 /* Text of the last error returned on the calling thread ("" if none). */

@@ -132,12 +132,22 @@ def test_prefill_chunk_argument_checks(lib):
 def test_prefill_chunk_workspace_formula(lib):
     """Rotated new keys [B,Hkv,n,D] and one cos/sin table per sequence
     [B,n,r/2] (each sequence starts at its own position), each rounded up to
-    256 bytes."""
+    256 bytes; plus the key-split partials [B,n,Hq,splits,D+4] fp32 when the
+    call splits (few rows over a long cache)."""
     Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
     r256 = lambda x: (x + 255) // 256 * 256
-    for B, n in ((1, 2048), (64, 4), (3, 7)):
-        want = r256(B * 8 * n * 128 * 2) + r256(B * n * 32 * 8)
-        assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), B, n) == want
+    base = lambda B, n: r256(B * 8 * n * 128 * 2) + r256(B * n * 32 * 8)
+    ws = lambda B, n, end: lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), B, n, end)
+    # enough rows to fill the chip (2048-token chunk, 512 blocks of 8 waves): no split
+    assert ws(1, 2048, 32768) == base(1, 2048)
+    assert ws(3, 7, 100) == base(3, 7)                       # short keys: no split
+    # a 1 + 3 verify step of 64 sequences up to 131072 keys: 512 blocks of 4
+    # waves, 2050 tiles cut into 4 splits of 513
+    assert ws(64, 4, 131072) == base(64, 4) + r256(64 * 4 * 64 * 4 * 132 * 4)
+    # one sequence: 8 blocks; at most 2050 / 16 = 128 splits, of 17 tiles,
+    # which 2050 tiles fill in 121 splits
+    assert ws(1, 4, 131072) == base(1, 4) + r256(1 * 4 * 64 * 121 * 132 * 4)
+    assert ws(1, 4, 3) == 0                                  # max_end_pos below n_new
 
 
 def test_kv_append_argument_checks(lib):
@@ -203,6 +213,7 @@ def test_tuning_overrides(lib):
     assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 157 * per_split
     assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, -1) == hgqa.EINVAL
     assert lib.hgqa_set_tuning(hgqa.TUNE_PREFILL_WAVES, 6) == hgqa.EINVAL
+    assert lib.hgqa_set_tuning(hgqa.TUNE_CHUNK_SPLIT_TILES, -5) == hgqa.EINVAL
     assert lib.hgqa_set_tuning(99, 0) == hgqa.EINVAL
     assert "knob" in hgqa.hgqa_last_error()
     for w in (4, 8, 0):

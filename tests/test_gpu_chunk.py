@@ -132,3 +132,31 @@ def test_chunks_in_sequence_equal_one_prefill():
     err = (chunked.float() - whole.float()).abs()
     print(f"chunked vs one call: max-abs {float(err.max()):.3e}", flush=True)
     assert float(err.max()) <= 1e-2
+
+
+# Key splits: each case again with the tiles per split forced small, so the
+# splits, the empty trailing splits of the shorter sequences and the merge
+# all run; results must match the oracle as without splits.
+SPLIT_CASES = [0, 3, 6, 11, 13, 14]
+
+
+@pytest.mark.parametrize("split_tiles", [1, 3, 7])
+@pytest.mark.parametrize("idx", SPLIT_CASES)
+def test_chunk_key_splits(idx, split_tiles, tuning):
+    require_gpu()
+    shape, dtype, p0, n = CASES[idx]
+    if dtype != hgqa.BF16:
+        pytest.skip("key splits are a bf16 path")
+    tuning(hgqa.TUNE_CHUNK_SPLIT_TILES, split_tiles)
+    _chunk_case(shape, dtype, p0, n, idx)
+
+
+def test_verify_step_automatic_splits():
+    """A 1 + 3 verify step of three sequences over a full cache of up to 9000
+    keys: 24 blocks, so the automatic plan splits the keys."""
+    require_gpu()
+    shape = LayerShape(FULL, 0, 64, 8, 128, 5e6, 0.5)
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    base = hgqa.attn_prefill_chunk_workspace_bytes(L, 3, 4, 4)  # no split for 4 keys
+    assert hgqa.attn_prefill_chunk_workspace_bytes(L, 3, 4, 9000) > base
+    _chunk_case(shape, hgqa.BF16, [8996, 5000, 123], 4, 40)
