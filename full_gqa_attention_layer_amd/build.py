@@ -56,5 +56,35 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the C-ABI
+# front end (device code is built as usual). The runtime is not linked in:
+# a process loads the library with the clang ASan runtime preloaded.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-shared-libsan"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that matches hipcc, or "" if absent."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("clang") or "/opt/rocm/llvm/bin/clang"
+    try:
+        path = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                              capture_output=True, text=True).stdout.strip()
+    except OSError:
+        return ""
+    return path if os.path.isabs(path) and os.path.exists(path) else ""
+
+
+def build_sanitized(out: str) -> str:
+    """libhgqa.so with its host code under ASan + UBSan, written to out."""
+    cmd = [c for c in command(out, SANITIZE_HOST) if c != "-Wl,-z,defs"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
