@@ -122,9 +122,21 @@ class ClockSampler:
     def __enter__(self):
         try:
             import amdsmi
+            import torch
             amdsmi.amdsmi_init()
             self._smi = amdsmi
-            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            # amdsmi lists every GPU of the node: take the one whose PCI address
+            # is this process's device 0
+            p = torch.cuda.get_device_properties(0)
+            want = (int(p.pci_domain_id), int(p.pci_bus_id), int(p.pci_device_id))
+            self._h = None
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self._h, self.bdf = h, bdf
+            if self._h is None:
+                raise RuntimeError(f"no amdsmi device at PCI {want}")
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         except Exception as e:  # noqa: BLE001 - the clock record is optional
@@ -164,7 +176,7 @@ class ClockSampler:
             v = sorted(v)
             return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
         return {"average_gfxclk_mhz": stats(self.avg), "current_gfxclk_mhz_xcd_mean": stats(self.cur),
-                "error": self.error,
+                "error": self.error, "pci": getattr(self, "bdf", None),
                 "source": "amdsmi GPU metrics, sampled every 10 ms during the block's timed steps"}
 
 
