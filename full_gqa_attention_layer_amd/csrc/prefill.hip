@@ -120,7 +120,8 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void
 
 constexpr int kCsFloat2 = 1024;  // cos/sin rows of one row block: 8 KB
 
-// One stage holds a K tile and a V tile. With 4 waves (128 rows), stage 1
+// One stage holds a K tile and a V tile; the kernel keeps its two stages as
+// two LDS objects (see the tile loop). With 4 waves (128 rows), stage 1
 // first holds the block's Q rows (128 x D bf16 = kBN x 2D) and stage 0
 // finally the output rows; with 8 waves (256 rows, one workgroup per CU) a
 // separate area holds first Q, then the output.
@@ -131,7 +132,6 @@ struct PrefillStage {
 };
 template <int D, int KW>
 struct PrefillLds {
-  PrefillStage<D> st[2];
   uint16_t qo[KW > 4 ? KW * kRowsPerWave * D : 8];
   float2 cs[KW > 4 ? 2 * kCsFloat2 : kCsFloat2];
 };
@@ -150,6 +150,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   constexpr int NS = D / 16;                  // k-steps of the score product
   constexpr int NDB = D / 32;                 // 32-wide d blocks of the output
   __shared__ PrefillLds<D, KW> sm;
+  __shared__ PrefillStage<D> stage0, stage1;
+  auto stg = [&](int i) -> PrefillStage<D>& { return i ? stage1 : stage0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -240,9 +242,10 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const size_t cache_head = kCache ? (size_t)(b * Hkv + kvh) * a.cap * D : 0;
 
   // HBM -> LDS without registers: each wave moves PER_WAVE 1 KB pieces of
-  // both tiles. Keys past the end re-read the last key: finite values that
-  // the causal mask hides (their probabilities are exactly 0). In a chunk,
-  // keys before p0 come from the cache: slot j, or j mod cap in a ring.
+  // both tiles. Keys past the end read as zeros (without a cache) or re-read
+  // the last key (in a chunk): finite values that the causal mask hides
+  // (their probabilities are exactly 0). In a chunk, keys before p0 come
+  // from the cache: slot j, or j mod cap in a ring.
   //
   // koff / voff are the byte offsets of this lane's pieces inside a tile, so
   // a whole tile (ending at or before the last key, wholly in the chunk or
@@ -262,7 +265,27 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   const uint32_t voff = 2u * (__umul24(key_l, (unsigned)vstride) + vswz);
   // V in a cache has rows D apart (a chunk's V rows are Hkv D apart).
   const uint32_t vcoff = 2u * ((uint32_t)key_l * D + vswz);
+  // Without a cache a tile is one descriptor pair ending at the sequence's
+  // last key (loads past it return zeros and touch no memory), so the copy
+  // has no branch; the bound is on the vector offset alone, so each V piece
+  // carries its own offset.
+  uint32_t voffs[PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < PER_WAVE; ++i) voffs[i] = voff + (uint32_t)(i * KPP) * (uint32_t)vstride * 2u;
   auto load_tile = [&](int j0, int st) {
+    if constexpr (!kCache) {
+      const int nk = min(kBN, j_last - j0 + 1);  // keys of the tile in the sequence, >= 1
+      const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kbase + (size_t)j0 * D, (uint32_t)(nk * D * 2));
+      const __amdgpu_buffer_rsrc_t vres =
+          tile_rsrc(vbase + (size_t)j0 * vstride, (uint32_t)(((nk - 1) * vstride + D) * 2));
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int I = wave * PER_WAVE + i;
+        copy16_to_lds(kres, (lds_void_t*)&stg(st).k[512 * I], koff[i], 0u);
+        copy16_to_lds(vres, (lds_void_t*)&stg(st).v[512 * I], voffs[i], 0u);
+      }
+      return;
+    }
     const int kmax = j_last - j0;
     // a whole tile through buffer descriptors: uniform bases, the lane
     // offsets above, no vector arithmetic
@@ -272,8 +295,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int I = wave * PER_WAVE + i;
-        copy16_to_lds(kres, (lds_void_t*)&sm.st[st].k[512 * I], koff[i], 0u);
-        copy16_to_lds(vres, (lds_void_t*)&sm.st[st].v[512 * I], vo, (uint32_t)i * KPP * vrow * 2);
+        copy16_to_lds(kres, (lds_void_t*)&stg(st).k[512 * I], koff[i], 0u);
+        copy16_to_lds(vres, (lds_void_t*)&stg(st).v[512 * I], vo, (uint32_t)i * KPP * vrow * 2);
       }
     };
     if (kmax >= kBN - 1 && j0 >= p0) {  // every key in this call's chunk
@@ -292,8 +315,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
       }
     }
     auto issue = [&](int I, const void* ksrc, const void* vsrc) {
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)&sm.st[st].k[512 * I], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)&sm.st[st].v[512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void_t*)&stg(st).k[512 * I], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, (lds_void_t*)&stg(st).v[512 * I], 16, 0, 0);
     };
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
@@ -319,7 +342,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   // fragment reads below are conflict-free.
   {
     constexpr int Q_PIECES = kRows * D * 2 / 1024 / kWaves;
-    uint16_t* qs = KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[1]);
+    uint16_t* qs = KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&stage1);
 #pragma unroll
     for (int i = 0; i < Q_PIECES; ++i) {
       const int I = wave * Q_PIECES + i;
@@ -367,7 +390,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   u32x4_t qraw[NS];
   {
     const int r = wave * kRowsPerWave + n;
-    const uint16_t* qs = (KW > 4 ? sm.qo : reinterpret_cast<const uint16_t*>(&sm.st[1])) + r * D;
+    const uint16_t* qs = (KW > 4 ? sm.qo : reinterpret_cast<const uint16_t*>(&stage1)) + r * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qraw[s] = *reinterpret_cast<const u32x4_t*>(qs + 8 * ((2 * s + g) ^ Swz<D>::k(r)));
@@ -445,12 +468,16 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
 
   // One K/V tile. NKB counts the 32-key halves computed: the upper half of a
   // wave's last tile often holds only keys past all its rows, and is skipped.
-  auto tile = [&](int it, auto nkb_tag, auto first_tag) {
+  // LOAD: the next tile is copied into the other stage during this one.
+  // STAGE: the stage this tile sits in, known at compile time.
+  auto tile = [&](int it, auto nkb_tag, auto first_tag, auto load_tag, auto stage_tag) {
     constexpr int NKB = decltype(nkb_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value;
-    const int st = it & 1;
+    constexpr bool LOAD = decltype(load_tag)::value;
+    constexpr int st = decltype(stage_tag)::value;
     const int j0 = j_lo + it * kBN;
-    if (it + 1 < ntiles) load_tile(j0 + kBN, st ^ 1);
+    // In a chunk the copy branches (chunk or cache, ring wrap): issue it first.
+    if constexpr (kCache && LOAD) load_tile(j0 + kBN, st ^ 1);
     if (kCache && !wave_rows) {
       // a chunk of a few tokens leaves whole waves without rows: they only
       // copy their share of the tiles (no products, no LDS fragment reads)
@@ -458,8 +485,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
       __syncthreads();
       return;
     }
-    const uint16_t* ks = sm.st[st].k;
-    const uint16_t* vs = sm.st[st].v;
+    const uint16_t* ks = stg(st).k;
+    const uint16_t* vs = stg(st).v;
 
     // S^T for two 32-key blocks, the blocks' products alternating; each K
     // fragment read runs RA products ahead of its product, so the LDS
@@ -467,6 +494,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     f32x16_t S[2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) S[kb] = FIRST ? f32x16_t{} : negm;
+    // Without a cache the copy has no branch and joins the products' schedule.
+    if constexpr (!kCache && LOAD) load_tile(j0 + kBN, st ^ 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -477,12 +506,18 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], S[kb], 0, 0, 0);
       }
     {
+      // The next tile's copy pieces go one after every second product. Issued
+      // together at the top of the tile, every wave of the CU queued on the
+      // copy path at once and no products ran meanwhile.
       constexpr int NM = NS * NKB, RA = 4 < NM ? 4 : NM;
+      constexpr int NC = (!kCache && LOAD) ? 2 * PER_WAVE : 0;
+      static_assert(NC == 0 || 2 * NC <= NM, "a copy piece after every second product");
       __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);  // the first RA fragment reads
 #pragma unroll
       for (int i = 0; i < NM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product
         if (i + RA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read RA ahead
+        if (i % 2 == 1 && i / 2 < NC) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // a copy
       }
     }
 
@@ -575,10 +610,27 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   using First = std::integral_constant<bool, true>;
   using Full = std::integral_constant<int, 2>;
   using Half = std::integral_constant<int, 1>;
-  if (ntiles > 1) tile(0, Full{}, First{});
-  for (int it = 1; it + 1 < ntiles; ++it) tile(it, Full{}, Later{});
-  if (j_lo + (ntiles - 1) * kBN + 32 > tw_hi) tile(ntiles - 1, Half{}, Later{});
-  else tile(ntiles - 1, Full{}, Later{});
+  using Load = std::integral_constant<bool, true>;
+  using NoLoad = std::integral_constant<bool, false>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // Unrolled by two, so that every copy of the tile body names its stages
+  // as distinct LDS objects: the compiler then lets the next tile's copies
+  // move among this tile's fragment reads, and waits for them only where a
+  // read could touch the stage being filled.
+  if (ntiles > 1) tile(0, Full{}, First{}, Load{}, S0{});
+  for (int it = 1; it + 1 < ntiles; it += 2) {
+    tile(it, Full{}, Later{}, Load{}, S1{});
+    if (it + 2 < ntiles) tile(it + 1, Full{}, Later{}, Load{}, S0{});
+  }
+  const bool last_half = j_lo + (ntiles - 1) * kBN + 32 > tw_hi;
+  if ((ntiles - 1) & 1) {
+    if (last_half) tile(ntiles - 1, Half{}, Later{}, NoLoad{}, S1{});
+    else tile(ntiles - 1, Full{}, Later{}, NoLoad{}, S1{});
+  } else {
+    if (last_half) tile(ntiles - 1, Half{}, Later{}, NoLoad{}, S0{});
+    else tile(ntiles - 1, Full{}, Later{}, NoLoad{}, S0{});
+  }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if constexpr (kCache) {
@@ -603,7 +655,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   // ended on a barrier with no load in flight, or with 8 waves the Q/output
   // area) so that the stores write whole rows.
   const float inv = row_ok ? sigmoidf_dev(gate_logit) / l_tot : 0.0f;
-  uint16_t* ow = (KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&sm.st[0])) + wave * (kRowsPerWave * D);  // this wave's rows
+  uint16_t* ow = (KW > 4 ? sm.qo : reinterpret_cast<uint16_t*>(&stage0)) + wave * (kRowsPerWave * D);  // this wave's rows
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
