@@ -8,15 +8,17 @@
 // "Muse-Glimmer-30B-6bit" walkthrough, "each layer: double LayerNorm + gated
 // attention".
 //
-// bf16 kernel (gfx950, MFMA): one workgroup of 4 waves owns 128 query rows of
-// one KV head, where a row is a (position, query head) pair with the G heads
-// of a position adjacent; every K/V tile staged in LDS therefore serves all G
-// query heads of its group. Each wave owns 32 rows and computes
+// bf16 kernel (gfx950, MFMA): one workgroup of 4 or 8 waves owns 128 or 256
+// query rows of one KV head, where a row is a (position, query head) pair with
+// the G heads of a position adjacent; every K/V tile staged in LDS therefore
+// serves all G query heads of its group. Each wave owns 32 rows and computes
 //   S^T = K_tile (64 keys x D) * Q^T (D x 32 rows)   v_mfma_f32_32x32x16_bf16
 //   O^T += V^T (D x 64 keys) * P^T (64 keys x 32 rows)
 // so the softmax probabilities leave the score accumulator already in the
-// B-operand layout of the second product. V is stored transposed in LDS with
-// its keys permuted to match. K arrives pre-rotated from the pre-pass; Q is
+// B-operand layout of the second product. V sits in LDS as rows and is read
+// transposed (ds_read_b64_tr_b16) in P's key order. Tiles move HBM -> LDS
+// through two stages, the next tile's copy interleaved with this tile's score
+// products, one barrier per tile. K arrives pre-rotated from the pre-pass; Q is
 // rotated while it is loaded, from the pre-pass's cos/sin table, and carries
 // the softmax scale in log2 units; the score accumulators start from minus
 // the row's softmax reference, so exp2 applies to them directly. Only tiles
