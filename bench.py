@@ -112,10 +112,12 @@ def window_ms(torch, fn, n):
 class ClockSampler:
     """GFX clock samples (MHz) from amdsmi's GPU metrics in a side thread while
     a timed region runs: the SMU's average GFX clock and the mean of the
-    per-XCD current clocks. Empty when amdsmi is not usable."""
+    per-XCD current clocks, with the socket power (W) and hotspot temperature
+    (C) beside them. Empty when amdsmi is not usable."""
 
     def __init__(self, period=0.01):
         self.period, self.avg, self.cur, self.error = period, [], [], None
+        self.power, self.temp, self.power_cap = [], [], None
         self._stop = threading.Event()
         self._thread = None
 
@@ -137,6 +139,10 @@ class ClockSampler:
                     self._h, self.bdf = h, bdf
             if self._h is None:
                 raise RuntimeError(f"no amdsmi device at PCI {want}")
+            try:
+                self.power_cap = amdsmi.amdsmi_get_power_cap_info(self._h)
+            except Exception:  # noqa: BLE001 - optional
+                self.power_cap = None
             self._thread = threading.Thread(target=self._run, daemon=True)
             self._thread.start()
         except Exception as e:  # noqa: BLE001 - the clock record is optional
@@ -155,6 +161,12 @@ class ClockSampler:
                 xcd = [num(x) for x in (m.get("current_gfxclks") or []) if num(x) is not None]
                 if xcd:
                     self.cur.append(sum(xcd) / len(xcd))
+                w = num(m.get("current_socket_power")) or num(m.get("average_socket_power"))
+                if w is not None:
+                    self.power.append(w)
+                t = num(m.get("temperature_hotspot"))
+                if t is not None:
+                    self.temp.append(t)
             except Exception as e:  # noqa: BLE001
                 self.error = repr(e)
                 return
@@ -174,10 +186,15 @@ class ClockSampler:
             if not v:
                 return None
             v = sorted(v)
-            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+            # one distinct value over many samples means the metrics table was
+            # not refreshed while the region ran (seen on some boxes)
+            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
+                    "distinct": len(set(v))}
         return {"average_gfxclk_mhz": stats(self.avg), "current_gfxclk_mhz_xcd_mean": stats(self.cur),
+                "socket_power_w": stats(self.power), "hotspot_temp_c": stats(self.temp),
+                "power_cap_info": self.power_cap,
                 "error": self.error, "pci": getattr(self, "bdf", None),
-                "source": "amdsmi GPU metrics, sampled every 10 ms during the block's timed steps"}
+                "source": "amdsmi GPU metrics, sampled every 10 ms during the timed region"}
 
 
 # ----------------------------------------------------------------- inputs
@@ -451,12 +468,13 @@ def bench_prefill(args, torch, hgqa, synth, workloads, acc):
         fn = lambda: hgqa.attn_prefill(L, q, k, v, g, out=out, workspace=ws)
         for _ in range(args.warmup):
             fn()
-        ms = window_ms(torch, fn, n)
+        with ClockSampler() as clk:
+            ms = window_ms(torch, fn, n)
         pf = acc.prefill_flops(B, T, shape.num_q_heads, shape.head_dim, shape.layer_type,
                                shape.window)
         tf = pf / (ms * 1e-3) / 1e12
         res[name] = {"ms": ms, "TFLOP/s": tf, "frac_mfma": tf / acc.PEAK_BF16_TFLOPS,
-                     "flops": pf, "workload": wl.name,
+                     "flops": pf, "workload": wl.name, "clocks": clk.summary(),
                      "timing": f"one HIP event pair around {n} back-to-back attn_prefill calls "
                                "(K pre-pass + attention kernel)"}
         log(f"prefill {name}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
