@@ -113,7 +113,8 @@ class ClockSampler:
     """GFX clock samples (MHz) from amdsmi's GPU metrics in a side thread while
     a timed region runs: the SMU's average GFX clock and the mean of the
     per-XCD current clocks, with the socket power (W) and hotspot temperature
-    (C) beside them. Empty when amdsmi is not usable."""
+    (C) beside them. Only readings of a refreshed metrics table count. Empty
+    when amdsmi is not usable."""
 
     def __init__(self, period=0.01):
         self.period, self.avg, self.cur, self.error = period, [], [], None
@@ -152,9 +153,22 @@ class ClockSampler:
     def _run(self):
         def num(x):
             return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+        # the SMU refreshes its metrics table on its own schedule: a reading
+        # counts only when the table's own timestamp has moved since the last
+        # one (and since the region started)
+        last = None
+        try:
+            last = self._smi.amdsmi_get_gpu_metrics_info(self._h).get("system_clock_counter")
+        except Exception:  # noqa: BLE001
+            pass
         while not self._stop.is_set():
             try:
                 m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                stamp = m.get("system_clock_counter")
+                if stamp is not None and stamp == last:
+                    time.sleep(self.period)
+                    continue
+                last = stamp
                 a = num(m.get("average_gfxclk_frequency"))
                 if a is not None:
                     self.avg.append(a)
@@ -186,8 +200,6 @@ class ClockSampler:
             if not v:
                 return None
             v = sorted(v)
-            # one distinct value over many samples means the metrics table was
-            # not refreshed while the region ran (seen on some boxes)
             return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v),
                     "distinct": len(set(v))}
         return {"average_gfxclk_mhz": stats(self.avg), "current_gfxclk_mhz_xcd_mean": stats(self.cur),
