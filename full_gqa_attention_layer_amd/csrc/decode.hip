@@ -300,9 +300,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
 
   // Chunks in pairs, two in flight: while chunk c is computed, chunk c + 1
   // is arriving; chunk c + 2 is requested into c's buffers once c is done.
-  // Every wave issues the same loads each pair, so the waits stay exact.
+  // Every wave issues the same loads each pair, so the waits stay exact. The
+  // last pair requests nothing more: requests past the split's keys would
+  // only put a round trip between the last chunk and the merge.
   const int nch = rel0 < nrel ? (nrel - rel0 + STEP - 1) / STEP : 0;
-  for (int pr = 0; pr < (nch + 1) / 2; ++pr) {
+  const int npairs = (nch + 1) / 2;
+  for (int pr = 0; pr + 1 < npairs; ++pr) {
     const int r = rel0 + 2 * pr * STEP;
     // Scheduling fences around each refill: the buffer's reads (consumed by
     // the products above) are done before its copies are issued, and the
@@ -319,10 +322,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     issue(r + 3 * STEP, kfb, vb_buf);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (npairs > 0) {
+    const int r = rel0 + 2 * (npairs - 1) * STEP;
+    vm_wait_keep<2 * NS + VDMA>();
+    compute(r, kfa, va_buf);
+    vm_wait_keep<0>();
+    compute(r + STEP, kfb, vb_buf);
+  }
 
   // ---- merge the waves of this workgroup
   const float l_w = rows_sum(l_run);
-  __builtin_amdgcn_s_waitcnt(0);  // the trailing copies into buffer a have landed
+  __builtin_amdgcn_s_waitcnt(0);  // nothing of this wave is still in flight
   __syncthreads();                // every wave is done with its buffer a (aliased below)
   if (g == 0) {
     sm.u.mg.m[n16][wave] = m_run;
