@@ -330,10 +330,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
     compute(r + STEP, kfb, vb_buf);
   }
 
-  // ---- merge the waves of this workgroup
+  // ---- merge the waves of this workgroup. A wave's output rows overlay
+  // exactly its own buffer a, and the maxima, sums and gates lie past every
+  // V buffer, so each wave writes them as soon as its own keys are done.
+  static_assert(sizeof(DecodeLds<D>::u.mg.o[0]) == sizeof(DecodeLds<D>::u.v[0]),
+                "a wave's output rows overlay its own V buffer");
+  static_assert(offsetof(DecodeLds<D>, u.mg.m) >= sizeof(DecodeLds<D>::u.v),
+                "the merge's maxima and sums lie past the V buffers");
   const float l_w = rows_sum(l_run);
   __builtin_amdgcn_s_waitcnt(0);  // nothing of this wave is still in flight
-  __syncthreads();                // every wave is done with its buffer a (aliased below)
   if (g == 0) {
     sm.u.mg.m[n16][wave] = m_run;
     sm.u.mg.l[n16][wave] = l_w;
