@@ -437,7 +437,7 @@ def bench_block(args, torch, hgqa, workloads, acc, block):
                        "frac_mfma": pf / (wms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS})
         log(f"block layer {li} ({kind}): {wms:.3f} ms, {layers[-1]['TFLOP/s']:.0f} TFLOP/s")
     full = layers[-1]
-    kernel = "prefill_bf16_kernel<128, false, 8, false> (+ its K pre-pass)"
+    kernel = "prefill_bf16_kernel<128, 0, 8, false> (+ its K pre-pass)"
     return {
         "ms_per_step": ms,
         "value": flops / (ms * 1e-3) / 1e12,

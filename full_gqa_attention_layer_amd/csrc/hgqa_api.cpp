@@ -362,7 +362,10 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
       return fail(HGQA_EINVAL, "a cache must not alias q, k, v, gate, out or the workspace");
   if (k_cache == v_cache) return fail(HGQA_EINVAL, "k_cache and v_cache must differ");
 
-  // Attention first: a ring still holds the W - 1 positions before the chunk.
+  // A ring still holds the W - 1 positions before the chunk, so there the
+  // attention runs first and the chunk joins the cache after it. A full
+  // layer's cache has a slot for every position: there the chunk is appended
+  // first and the attention reads every key from the cache (bf16, D = 128).
   hgqa::PrefillArgs a = prefill_args(l, batch, n_new, q, k, v, gate, out, workspace);
   if (plan_splits(l, a, max_end_pos) > 0)
     a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + chunk_ws(l, batch, n_new));
@@ -373,11 +376,10 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
   a.v_cache = v_cache;
   a.cap = cache_capacity;
   a.ring = l.sliding;
+  a.keys_in_cache = !l.sliding && l.elem == hgqa::Elem::BF16 && l.D == 128;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hgqa::launch_prefill(a, l.elem, s);
-  if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
 
-  // Then the chunk joins the cache, as kv_append would leave it.
+  // The chunk joins the cache, as kv_append would leave it.
   hgqa::AppendArgs ap{};
   ap.start_pos = start_pos;
   ap.k_new = k;
@@ -392,8 +394,17 @@ int attn_prefill_chunk(const hgqa_layer* layer, int32_t batch, int32_t n_new,
   ap.sliding = l.sliding;
   ap.window = l.window;
   ap.rope = a.rope;
-  e = hgqa::launch_kv_append(ap, l.elem, s);
-  if (e != hipSuccess) return fail(HGQA_EHIP, "kv_append launch failed: %s", hipGetErrorString(e));
+  hipError_t e;
+  if (a.keys_in_cache) {
+    e = hgqa::launch_kv_append(ap, l.elem, s);
+    if (e != hipSuccess) return fail(HGQA_EHIP, "kv_append launch failed: %s", hipGetErrorString(e));
+  }
+  e = hgqa::launch_prefill(a, l.elem, s);
+  if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
+  if (!a.keys_in_cache) {
+    e = hgqa::launch_kv_append(ap, l.elem, s);
+    if (e != hipSuccess) return fail(HGQA_EHIP, "kv_append launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

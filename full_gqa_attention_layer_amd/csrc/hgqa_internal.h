@@ -46,6 +46,10 @@ struct PrefillArgs {
   const void* k_cache;
   const void* v_cache;
   int cap, ring;
+  // Full-layer chunk whose new keys were appended before the attention: every
+  // key, the chunk's too, is read from the cache (slot p), and the pre-pass
+  // only writes the cos/sin rows.
+  int keys_in_cache;
   int waves;            // bf16 workgroup shape override: 0 automatic, 4 or 8
   // Split over keys (chunks only): each row block's key tiles are cut into
   // num_splits runs of split_tiles; each run writes per-row partials

@@ -138,10 +138,12 @@ struct PrefillLds {
   float2 cs[KW > 4 ? 2 * kCsFloat2 : kCsFloat2];
 };
 
-// kCache: chunked prefill, keys before position p0 come from the cache.
+// kCache: 0 for a prompt; 1 for a chunk, keys before position p0 from the
+// cache and the chunk's own keys from k and v; 2 for a chunk of a full layer
+// that was appended first, every key from the cache.
 // KW: waves per workgroup (4: two workgroups per CU; 8: one, every K/V tile
 // serving twice the rows). SL: sliding-window mask (else causal only).
-template <int D, bool kCache, int KW, bool SL>
+template <int D, int kCache, int KW, bool SL>
 __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int kWaves = KW;
   constexpr int kRows = kWaves * kRowsPerWave;  // query rows per workgroup
@@ -275,6 +277,24 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) voffs[i] = voff + (uint32_t)(i * KPP) * (uint32_t)vstride * 2u;
   auto load_tile = [&](int j0, int st) {
+    if constexpr (kCache == 2) {
+      // cache slots j0.. of this sequence and KV head, rows D apart; the
+      // descriptors end at the chunk's last key
+      const int nk = min(kBN, j_last - j0 + 1);
+      const size_t off = cache_head + (size_t)j0 * D;
+      const __amdgpu_buffer_rsrc_t kres =
+          tile_rsrc(static_cast<const uint16_t*>(a.k_cache) + off, (uint32_t)(nk * D * 2));
+      const __amdgpu_buffer_rsrc_t vres =
+          tile_rsrc(static_cast<const uint16_t*>(a.v_cache) + off, (uint32_t)(nk * D * 2));
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int I = wave * PER_WAVE + i;
+        copy16_to_lds(kres, (lds_void_t*)&stg(st).k[512 * I], koff[i], 0u);
+        copy16_to_lds(vres, (lds_void_t*)&stg(st).v[512 * I],
+                      vcoff + (uint32_t)(i * KPP * D * 2), 0u);
+      }
+      return;
+    }
     if constexpr (!kCache) {
       const int nk = min(kBN, j_last - j0 + 1);  // keys of the tile in the sequence, >= 1
       const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kbase + (size_t)j0 * D, (uint32_t)(nk * D * 2));
@@ -478,11 +498,16 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     constexpr bool LOAD = decltype(load_tag)::value;
     constexpr int st = decltype(stage_tag)::value;
     const int j0 = j_lo + it * kBN;
-    // In a chunk the copy branches (chunk or cache, ring wrap): issue it first.
-    if constexpr (kCache && LOAD) load_tile(j0 + kBN, st ^ 1);
+    // A chunk over the cache and its own keys branches (chunk or cache, ring
+    // wrap): issue it first.
+    if constexpr (kCache == 1 && LOAD) load_tile(j0 + kBN, st ^ 1);
     if (kCache && !wave_rows) {
       // a chunk of a few tokens leaves whole waves without rows: they only
       // copy their share of the tiles (no products, no LDS fragment reads)
+      // (the empty asm keeps the compiler from hoisting this copy, identical
+      // to the one in the products' schedule below, above the branch)
+      asm volatile("" ::: "memory");
+      if constexpr (kCache == 2 && LOAD) load_tile(j0 + kBN, st ^ 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       return;
@@ -496,8 +521,8 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     f32x16_t S[2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) S[kb] = FIRST ? f32x16_t{} : negm;
-    // Without a cache the copy has no branch and joins the products' schedule.
-    if constexpr (!kCache && LOAD) load_tile(j0 + kBN, st ^ 1);
+    // Otherwise the copy has no branch and joins the products' schedule.
+    if constexpr (kCache != 1 && LOAD) load_tile(j0 + kBN, st ^ 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -512,7 +537,7 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
       // together at the top of the tile, every wave of the CU queued on the
       // copy path at once and no products ran meanwhile.
       constexpr int NM = NS * NKB, RA = 4 < NM ? 4 : NM;
-      constexpr int NC = (!kCache && LOAD) ? 2 * PER_WAVE : 0;
+      constexpr int NC = (kCache != 1 && LOAD) ? 2 * PER_WAVE : 0;
       static_assert(NC == 0 || 2 * NC <= NM, "a copy piece after every second product");
       __builtin_amdgcn_sched_group_barrier(0x100, RA, 0);  // the first RA fragment reads
 #pragma unroll
@@ -793,7 +818,7 @@ static int prefill_waves(const PrefillArgs& a) {
   return long_span && enough_rows ? 8 : 4;
 }
 
-template <int D, bool kCache, int KW>
+template <int D, int kCache, int KW>
 static void launch_bf16(const PrefillArgs& a, dim3 grid, hipStream_t s) {
   if (a.sliding)
     hipLaunchKernelGGL((prefill_bf16_kernel<D, kCache, KW, true>), grid, dim3(KW * 64), 0, s, a);
@@ -850,14 +875,19 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   const long long rows = (long long)kw * kRowsPerWave;
   const long long blocks = (TG + rows - 1) / rows * a.B * a.Hkv * (cache ? a.num_splits : 1);
   const dim3 grid((unsigned)blocks);
-  if (a.D == 128) {
-    if (cache && kw == 8) launch_bf16<128, true, 8>(a, grid, s);
-    else if (cache) launch_bf16<128, true, 4>(a, grid, s);
-    else if (kw == 8) launch_bf16<128, false, 8>(a, grid, s);
-    else launch_bf16<128, false, 4>(a, grid, s);
+  if (a.D == 128 && cache && a.keys_in_cache) {  // full layers only
+    if (kw == 8)
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, 8, false>), grid, dim3(8 * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_bf16_kernel<128, 2, 4, false>), grid, dim3(4 * 64), 0, s, a);
+  } else if (a.D == 128) {
+    if (cache && kw == 8) launch_bf16<128, 1, 8>(a, grid, s);
+    else if (cache) launch_bf16<128, 1, 4>(a, grid, s);
+    else if (kw == 8) launch_bf16<128, 0, 8>(a, grid, s);
+    else launch_bf16<128, 0, 4>(a, grid, s);
   } else {
-    if (cache) launch_bf16<64, true, 4>(a, grid, s);
-    else launch_bf16<64, false, 4>(a, grid, s);
+    if (cache) launch_bf16<64, 1, 4>(a, grid, s);
+    else launch_bf16<64, 0, 4>(a, grid, s);
   }
   err = hipGetLastError();
   if (err != hipSuccess || !cache || a.num_splits <= 1) return err;

@@ -97,7 +97,9 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
   uint16_t* kr = static_cast<uint16_t*>(a.k_rot);
   const int Hkv = a.Hkv;
   const int per_pos = Hkv * CH;
-  const int total = np * per_pos;
+  // a chunk appended before its attention reads K from the cache: only the
+  // cos/sin rows are needed
+  const int total = a.keys_in_cache ? 0 : np * per_pos;
 
   // chunk e: position t0 + tp, head h, dims d0..d0+7; its source row and the
   // partner chunk's offset (the chunk itself when it is not rotated)
@@ -116,9 +118,9 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
   const int e0 = threadIdx.x, e1 = threadIdx.x + 256;
   const double f0 = e0 < ntrig ? a.rope.freq_over_pi[e0 % max(half, 1)] : 0.0;
   const double f1 = e1 < ntrig ? a.rope.freq_over_pi[e1 % max(half, 1)] : 0.0;
-  u32x4_t raw[kPrefetch], praw[kPrefetch];
+  u32x4_t raw[kPrefetch] = {}, praw[kPrefetch] = {};
 #pragma unroll
-  for (int c = 0; c < kPrefetch; ++c) {
+  for (int c = 0; c < (total > 0 ? kPrefetch : 0); ++c) {
     // clamped, so the loads form one straight run (a thread past the end
     // re-reads the last chunk and stores nothing)
     const int e = min((int)threadIdx.x + 256 * c, total - 1);
