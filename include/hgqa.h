@@ -177,8 +177,10 @@ size_t attn_prefill_chunk_workspace_bytes(const hgqa_layer* layer, int32_t batch
  *         start_pos[b] (every earlier position the new rows can see).
  *   out   [B, n, Hq, D]   gated attention output
  *   workspace            >= attn_prefill_chunk_workspace_bytes(layer, B, n)
- * In stream order the attention reads the cache before the append writes it,
- * so a ring may be overwritten by its own chunk. The caches must not alias any
+ * On a sliding layer the attention reads the ring before the append writes
+ * it (in stream order), so a ring may be overwritten by its own chunk; on a
+ * full layer (bf16, D = 128) the chunk is appended first and every key is
+ * read from the cache, which gives the same result. The caches must not alias any
  * other argument. n_new == 0 or batch == 0 does nothing. Errors: as
  * attn_prefill, plus HGQA_ENOSPACE when a full cache is smaller than
  * max_end_pos and HGQA_EINVAL when a ring's capacity differs from W. A
