@@ -133,8 +133,14 @@ constexpr long long kMaxElems = 1LL << 40;
 size_t rotated_k_bytes(const Layer& l, int B, int T) {
   return round256((size_t)B * l.Hkv * T * l.D * l.esize);
 }
+bool uses_vt(const Layer& l) { return !l.sliding && l.elem == hgqa::Elem::BF16 && l.D == 128; }
+int t_pad(int T) { return (T + 63) / 64 * 64; }
+size_t table_bytes(const Layer& l, int T) { return round256((size_t)T * l.half * sizeof(float2)); }
+size_t vt_bytes(const Layer& l, int B, int T) {
+  return uses_vt(l) ? round256((size_t)B * l.Hkv * l.D * t_pad(T) * sizeof(uint16_t)) : 0;
+}
 size_t prefill_ws(const Layer& l, int B, int T) {
-  return rotated_k_bytes(l, B, T) + round256((size_t)T * l.half * sizeof(float2));
+  return rotated_k_bytes(l, B, T) + table_bytes(l, T) + vt_bytes(l, B, T);
 }
 size_t chunk_ws(const Layer& l, int B, int T) {
   return rotated_k_bytes(l, B, T) + round256((size_t)B * T * l.half * sizeof(float2));
@@ -317,6 +323,11 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
                           prefill_ws(l, batch, seq_len));
   if (rc != HGQA_OK) return rc;
   hgqa::PrefillArgs a = prefill_args(l, batch, seq_len, q, k, v, gate, out, workspace);
+  if (uses_vt(l)) {
+    a.v_t = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
+                                        rotated_k_bytes(l, batch, seq_len) + table_bytes(l, seq_len));
+    a.t_pad = t_pad(seq_len);
+  }
   hipError_t e = hgqa::launch_prefill(a, l.elem, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(HGQA_EHIP, "prefill launch failed: %s", hipGetErrorString(e));
   return ok();

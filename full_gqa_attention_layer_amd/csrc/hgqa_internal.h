@@ -31,6 +31,13 @@ struct PrefillArgs {
   void* out;            // [B,T,Hq,D]
   void* k_rot;          // workspace: [B,Hkv,T,D] rotated K
   float2* cs_table;     // workspace: [T, half] (cos, sin), or [B, T, half] for chunks
+  // A prompt on a full bf16 layer with D = 128: V transposed by the pre-pass,
+  // [B, Hkv, D, t_pad] (t_pad = T rounded up to 64, keys past T zero), the
+  // keys of each 16-key group in the order the PV product takes them (0-3,
+  // 8-11, 4-7, 12-15), so one 16-byte LDS read feeds a product. Null
+  // otherwise.
+  uint16_t* v_t;
+  int t_pad;
   size_t cs_bstride;    // float2 entries between sequences' tables (0: one shared table)
   int B, T, Hq, Hkv, G, D;
   int sliding, window;

@@ -59,6 +59,12 @@ template <> struct Swz<64> {   // 32-dword rows: odd rows sit 32 banks over
   static __device__ __forceinline__ int k(int key) { return (key >> 1) & 7; }
   static __device__ __forceinline__ int v(int key) { return 4 * ((key >> 1) & 1); }
 };
+// A V^T tile sits as [128 dims][64 slots] bf16 rows (128 bytes: odd rows 32
+// banks over); chunk c of row dim is stored at position c ^ ((dim >> 1) & 7),
+// so 16 lanes reading one chunk of 16 consecutive dims hit distinct banks.
+struct SwzT {
+  static __device__ __forceinline__ int c(int dim) { return (dim >> 1) & 7; }
+};
 
 __device__ __forceinline__ void unpack8(u32x4_t raw, float (&x)[8]) {
 #pragma unroll
@@ -276,6 +282,20 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
   uint32_t voffs[PER_WAVE];
 #pragma unroll
   for (int i = 0; i < PER_WAVE; ++i) voffs[i] = voff + (uint32_t)(i * KPP) * (uint32_t)vstride * 2u;
+  // A full layer's prompt reads V^T rows (one per dim, t_pad slots) instead:
+  // a 1 KB piece holds 8 dims x 64 slots; lane l copies dim 8 piece + l / 8,
+  // and its 16 bytes land at chunk position l % 8, which holds source chunk
+  // (l % 8) ^ SwzT(dim).
+  constexpr bool VT = kCache == 0 && !SL && D == 128;
+  uint32_t vtoffs[VT ? PER_WAVE : 1];
+  if constexpr (VT) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int dim = 8 * (wave * PER_WAVE + i) + (lane >> 3);
+      vtoffs[i] = 2u * ((uint32_t)dim * (uint32_t)a.t_pad + 8u * (uint32_t)((lane & 7) ^ SwzT::c(dim)));
+    }
+  }
+  const uint16_t* vt_head = VT ? a.v_t + (size_t)(b * Hkv + kvh) * D * a.t_pad : nullptr;
   auto load_tile = [&](int j0, int st) {
     if constexpr (kCache == 2) {
       // cache slots j0.. of this sequence and KV head, rows D apart; the
@@ -298,13 +318,15 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
     if constexpr (!kCache) {
       const int nk = min(kBN, j_last - j0 + 1);  // keys of the tile in the sequence, >= 1
       const __amdgpu_buffer_rsrc_t kres = tile_rsrc(kbase + (size_t)j0 * D, (uint32_t)(nk * D * 2));
+      // (V^T: tiles start at multiples of 64, so a tile never runs past t_pad)
       const __amdgpu_buffer_rsrc_t vres =
-          tile_rsrc(vbase + (size_t)j0 * vstride, (uint32_t)(((nk - 1) * vstride + D) * 2));
+          VT ? tile_rsrc(vt_head + j0, (uint32_t)((D * a.t_pad - j0) * 2))
+             : tile_rsrc(vbase + (size_t)j0 * vstride, (uint32_t)(((nk - 1) * vstride + D) * 2));
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int I = wave * PER_WAVE + i;
         copy16_to_lds(kres, (lds_void_t*)&stg(st).k[512 * I], koff[i], 0u);
-        copy16_to_lds(vres, (lds_void_t*)&stg(st).v[512 * I], voffs[i], 0u);
+        copy16_to_lds(vres, (lds_void_t*)&stg(st).v[512 * I], VT ? vtoffs[VT ? i : 0] : voffs[i], 0u);
       }
       return;
     }
@@ -608,20 +630,28 @@ __global__ __launch_bounds__(KW * 64, 8 / KW) void prefill_bf16_kernel(PrefillAr
       }
     }
 
-    // O^T += V^T P^T, 4 k-steps of 16 keys; V^T comes transposed out of LDS.
+    // O^T += V^T P^T, 4 k-steps of 16 keys; V^T comes transposed out of LDS
+    // (or, from a V^T tile, straight: lane l reads dim l % 32 of the block,
+    // chunk 2 ks4 + l / 32, the eight keys P's lane holds for that k-half).
 #pragma unroll
     for (int ks4 = 0; ks4 < 2 * NKB; ++ks4) {
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pk[ks4]);
       const int k0 = 16 * ks4 + vkey0, k1 = k0 + 8;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int d = 32 * db + vd;
-        const int c = d >> 3, hw = d & 7;
-        const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(vs + k0 * D + 8 * (c ^ Swz<D>::v(k0)) + hw));
-        const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_t*)(vs + k1 * D + 8 * (c ^ Swz<D>::v(k1)) + hw));
-        const i16x8_t va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        i16x8_t va;
+        if constexpr (VT) {
+          const int dim = 32 * db + n, c = 2 * ks4 + g;
+          va = *reinterpret_cast<const i16x8_t*>(vs + dim * kBN + 8 * (c ^ SwzT::c(dim)));
+        } else {
+          const int d = 32 * db + vd;
+          const int c = d >> 3, hw = d & 7;
+          const i16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(vs + k0 * D + 8 * (c ^ Swz<D>::v(k0)) + hw));
+          const i16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t*)(vs + k1 * D + 8 * (c ^ Swz<D>::v(k1)) + hw));
+          va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va), pb,
                                                          O[db], 0, 0, 0);
       }

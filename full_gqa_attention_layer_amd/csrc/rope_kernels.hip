@@ -98,8 +98,8 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
   const int Hkv = a.Hkv;
   const int per_pos = Hkv * CH;
   // a chunk appended before its attention reads K from the cache: only the
-  // cos/sin rows are needed
-  const int total = a.keys_in_cache ? 0 : np * per_pos;
+  // cos/sin rows are needed (and a block past T only pads the V^T rows)
+  const int total = (a.keys_in_cache || np <= 0) ? 0 : np * per_pos;
 
   // chunk e: position t0 + tp, head h, dims d0..d0+7; its source row and the
   // partner chunk's offset (the chunk itself when it is not rotated)
@@ -174,10 +174,35 @@ __global__ __launch_bounds__(256) void prefill_rope_prepass_bf16(PrefillArgs a) 
     rotate_store(e, *reinterpret_cast<const u32x4_t*>(row + d0),
                  *reinterpret_cast<const u32x4_t*>(row + partner(d0)));
   }
+
+  // V^T rows for this block's 8 positions (zeros past T): keys t0 .. t0 + 7
+  // are one half of a 16-key group, whose slots hold keys 0-3, 8-11, 4-7,
+  // 12-15, so this half's first four keys go to slots 4 hf .. and its last
+  // four to slots 8 + 4 hf ..
+  if (a.v_t) {
+    const uint16_t* v = static_cast<const uint16_t*>(a.v);
+    const int grp = t0 >> 4, hf = (t0 >> 3) & 1;
+    for (int e = threadIdx.x; e < Hkv * D; e += blockDim.x) {
+      const int h = e / D, d = e - h * D;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ta = t0 + 2 * i, tb = ta + 1;
+        const uint32_t lo = ta < a.T ? v[(((size_t)b * a.T + ta) * Hkv + h) * D + d] : 0u;
+        const uint32_t hi = tb < a.T ? v[(((size_t)b * a.T + tb) * Hkv + h) * D + d] : 0u;
+        w[i] = lo | (hi << 16);
+      }
+      uint16_t* row = a.v_t + (((size_t)b * Hkv + h) * D + d) * a.t_pad + 16 * grp;
+      *reinterpret_cast<u32x2_t*>(row + 4 * hf) = u32x2_t{w[0], w[1]};
+      *reinterpret_cast<u32x2_t*>(row + 8 + 4 * hf) = u32x2_t{w[2], w[3]};
+    }
+  }
 }
 
 hipError_t launch_prefill_prepass(const PrefillArgs& a, Elem e, hipStream_t s) {
-  dim3 grid((a.T + kPrepassPositions - 1) / kPrepassPositions, a.B);
+  // with V^T the blocks run to t_pad, so its padding keys are written as zeros
+  const int tn = a.v_t ? a.t_pad : a.T;
+  dim3 grid((tn + kPrepassPositions - 1) / kPrepassPositions, a.B);
   if (e == Elem::F32)
     hipLaunchKernelGGL(prefill_rope_prepass<float>, grid, dim3(256), 0, s, a);
   else if (a.D == 128)

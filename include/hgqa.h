@@ -118,8 +118,10 @@ typedef struct {
 
 /*
  * Scratch bytes attn_prefill needs for this layer and shape: the rotated K,
- * [B, Hkv, T, D] in the layer dtype, and a cos/sin table [T, r/2] of float
- * pairs, each part rounded up to 256 bytes. Returns 0 for an invalid layer.
+ * [B, Hkv, T, D] in the layer dtype, a cos/sin table [T, r/2] of float pairs
+ * and, for a full bf16 layer with D = 128, V transposed, [B, Hkv, D, T'] bf16
+ * with T' = T rounded up to 64; each part rounded up to 256 bytes. Returns 0
+ * for an invalid layer.
  */
 size_t attn_prefill_workspace_bytes(const hgqa_layer* layer, int32_t batch,
                                     int32_t seq_len);

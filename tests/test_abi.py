@@ -104,6 +104,10 @@ def test_prefill_workspace_formula(lib):
     L = hgqa.layer(1, 512, 96, 12, 128, 1e4)
     # rotated K [B,Hkv,T,D] bf16 + cos/sin table [T, r/2] float pairs
     assert lib.attn_prefill_workspace_bytes(ctypes.byref(L), 1, 8192) == 8192 * 8 * 128 * 2 + 8192 * 64 * 8
+    # a full bf16 layer (D = 128) adds V^T [B,Hkv,D,T'] bf16, T' = T rounded up to 64
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    assert lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 2, 1000) == (
+        2 * 8 * 1000 * 128 * 2 + 1000 * 32 * 8 + 2 * 8 * 128 * 1024 * 2)
     Lf = hgqa.layer(0, 0, 4, 4, 64, 1e4, 1.0, 0.0, hgqa.FP32)
     assert lib.attn_prefill_workspace_bytes(ctypes.byref(Lf), 1, 256) == 256 * 64 * 4 + 256 * 32 * 8
 
