@@ -437,7 +437,7 @@ def bench_block(args, torch, hgqa, workloads, acc, block):
                        "frac_mfma": pf / (wms * 1e-3) / 1e12 / acc.PEAK_BF16_TFLOPS})
         log(f"block layer {li} ({kind}): {wms:.3f} ms, {layers[-1]['TFLOP/s']:.0f} TFLOP/s")
     full = layers[-1]
-    kernel = "prefill_bf16_kernel<128, 0, 8, false> (+ its K pre-pass)"
+    kernel = "prefill_bf16_kernel<128, 0, 8, false> (+ its pre-pass: rotated K, cos/sin rows, V^T)"
     return {
         "ms_per_step": ms,
         "value": flops / (ms * 1e-3) / 1e12,
@@ -488,7 +488,7 @@ def bench_prefill(args, torch, hgqa, synth, workloads, acc):
         res[name] = {"ms": ms, "TFLOP/s": tf, "frac_mfma": tf / acc.PEAK_BF16_TFLOPS,
                      "flops": pf, "workload": wl.name, "clocks": clk.summary(),
                      "timing": f"one HIP event pair around {n} back-to-back attn_prefill calls "
-                               "(K pre-pass + attention kernel)"}
+                               "(pre-pass + attention kernel)"}
         log(f"prefill {name}: {ms:.3f} ms, {tf:.0f} TFLOP/s")
         del q, k, v, g, out, ws
         torch.cuda.empty_cache()
