@@ -133,11 +133,16 @@ constexpr long long kMaxElems = 1LL << 40;
 size_t rotated_k_bytes(const Layer& l, int B, int T) {
   return round256((size_t)B * l.Hkv * T * l.D * l.esize);
 }
-bool uses_vt(const Layer& l) { return !l.sliding && l.elem == hgqa::Elem::BF16 && l.D == 128; }
 int t_pad(int T) { return (T + 63) / 64 * 64; }
+// V^T for full bf16 layers with D = 128, while one head's V^T rows stay
+// within the 32-bit byte offsets of a buffer descriptor
+bool uses_vt(const Layer& l, int T) {
+  return !l.sliding && l.elem == hgqa::Elem::BF16 && l.D == 128 &&
+         (long long)l.D * t_pad(T) * 2 < (1LL << 31);
+}
 size_t table_bytes(const Layer& l, int T) { return round256((size_t)T * l.half * sizeof(float2)); }
 size_t vt_bytes(const Layer& l, int B, int T) {
-  return uses_vt(l) ? round256((size_t)B * l.Hkv * l.D * t_pad(T) * sizeof(uint16_t)) : 0;
+  return uses_vt(l, T) ? round256((size_t)B * l.Hkv * l.D * t_pad(T) * sizeof(uint16_t)) : 0;
 }
 size_t prefill_ws(const Layer& l, int B, int T) {
   return rotated_k_bytes(l, B, T) + table_bytes(l, T) + vt_bytes(l, B, T);
@@ -319,11 +324,14 @@ int attn_prefill(const hgqa_layer* layer, int32_t batch, int32_t seq_len, const 
   if (rc != HGQA_OK) return rc;
   if (batch < 0 || seq_len < 0) return fail(HGQA_EINVAL, "batch and seq_len must be >= 0");
   if (batch == 0 || seq_len == 0) return ok();
+  if (!l.sliding && l.elem == hgqa::Elem::BF16 && l.D == 128 && !uses_vt(l, seq_len))
+    return fail(HGQA_EUNSUPPORTED, "a full-layer prompt of %d positions exceeds the V^T limit (2^23)",
+                seq_len);
   rc = check_prefill_call(l, batch, seq_len, q, k, v, gate, out, workspace, workspace_bytes,
                           prefill_ws(l, batch, seq_len));
   if (rc != HGQA_OK) return rc;
   hgqa::PrefillArgs a = prefill_args(l, batch, seq_len, q, k, v, gate, out, workspace);
-  if (uses_vt(l)) {
+  if (uses_vt(l, seq_len)) {
     a.v_t = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) +
                                         rotated_k_bytes(l, batch, seq_len) + table_bytes(l, seq_len));
     a.t_pad = t_pad(seq_len);

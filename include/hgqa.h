@@ -133,7 +133,9 @@ size_t attn_prefill_workspace_bytes(const hgqa_layer* layer, int32_t batch,
  *   gate  [B, T, Hq]      gate logits
  *   out   [B, T, Hq, D]   gated attention output
  *   workspace            >= attn_prefill_workspace_bytes(layer, B, T) bytes
- * batch == 0 or seq_len == 0 is a valid call that does nothing.
+ * batch == 0 or seq_len == 0 is a valid call that does nothing. A full bf16
+ * layer with D = 128 takes seq_len < 2^23 (HGQA_EUNSUPPORTED otherwise: its
+ * V^T rows must stay within 32-bit byte offsets).
  * The masks follow "Step-3.7-Flash-oQ3e" walkthrough 2.2; RoPE and the gate
  * follow 2.3 of the same page.
  */

@@ -100,6 +100,16 @@ def test_prefill_argument_checks(lib):
     assert lib.attn_prefill(None, 1, 16, z, z, z, z, z, z, 0, None) == hgqa.EINVAL
 
 
+def test_full_layer_prompt_length_limit(lib):
+    """A full bf16 layer with D = 128 keeps one head's V^T rows within 32-bit
+    byte offsets: seq_len 2^23 is refused before any pointer is looked at."""
+    L = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    assert _call_prefill(lib, L, T=1 << 23) == hgqa.EUNSUPPORTED
+    assert "V^T" in hgqa.hgqa_last_error()
+    Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)   # sliding: no V^T, no such limit
+    assert _call_prefill(lib, Ls, T=1 << 23, ws=1) == hgqa.ENOSPACE
+
+
 def test_prefill_workspace_formula(lib):
     L = hgqa.layer(1, 512, 96, 12, 128, 1e4)
     # rotated K [B,Hkv,T,D] bf16 + cos/sin table [T, r/2] float pairs
