@@ -24,6 +24,7 @@ constexpr int kDecWaves = 4;
 constexpr int kDecThreads = kDecWaves * 64;
 constexpr int kChunk = 32;
 constexpr int kDecMinKeysPerBlock = 1024;
+constexpr int kDecMinKeysFewPairs = 512;
 constexpr int kDecTargetBlocks = 2048;
 constexpr float kLog2eDec = 1.4426950408889634f;
 
@@ -388,37 +389,79 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
 }
 
 // Log-sum-exp merge of the splits of one (sequence, head), then the gate.
-// grid B*Hq, block D.
-template <typename T>
-__global__ void decode_merge_kernel(DecodeArgs a) {
+// A long context alone can have hundreds of splits (a single sequence of
+// 64K keys on two KV heads: 129), so the splits are spread over the threads
+// too: one block per (sequence, head, 32 dims) of 16 x NG threads, where
+// thread t takes dims 2 (t % 16) and 2 (t % 16) + 1 of its 32 and every
+// NG-th split from t / 16; the NG split groups then add up through LDS. NG
+// (4, 8 or 16) follows the call's split count.
+constexpr int kMergeDims = 32;
+constexpr int kMergeMaxThreads = 256;
+__global__ __launch_bounds__(kMergeMaxThreads) void decode_merge_kernel(DecodeArgs a) {
+  __shared__ float wave_max[kMergeMaxThreads / 64];
+  __shared__ float2 gacc[kMergeMaxThreads];
+  __shared__ float gsum[kMergeMaxThreads];
+  constexpr int DP = kMergeDims / 2;  // dim pairs per block
+  const int D = a.D, nq = D / kMergeDims;
   const int id = blockIdx.x;
-  const int b = id / a.Hq, h = id - (id / a.Hq) * a.Hq;
-  const int D = a.D, d = threadIdx.x;
+  const int bh = id / nq, dq = id - bh * nq;
+  const int b = bh / a.Hq;
+  const int tid = threadIdx.x, nt = blockDim.x, ng = nt / DP;
   int L = a.seq_lens[b];
   L = max(1, min(L, a.max_seq_len));
   const int n_vis = a.sliding ? min(L, a.window) : L;
   const int ns = (n_vis + a.split_keys - 1) / a.split_keys;
-  const float* part = a.partial + ((size_t)b * a.Hq + h) * a.num_splits * (D + 2);
+  const int rec = D + 2;  // a split's record: D outputs, its reference, its sum
+  const float* part = a.partial + (size_t)bh * a.num_splits * rec;
+
+  // the largest reference over the splits (every split holds a visible key)
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-  float acc = 0.0f, lsum = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float* p = part + s * (D + 2);
-    const float f = __builtin_amdgcn_exp2f(p[D] - M);
-    acc = fmaf(p[d], f, acc);
-    lsum = fmaf(p[D + 1], f, lsum);
+  for (int s = tid; s < ns; s += nt) M = fmaxf(M, part[(size_t)s * rec + D]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = M;
+  __syncthreads();
+  M = wave_max[0];
+  for (int w = 1; w < nt / 64; ++w) M = fmaxf(M, wave_max[w]);
+
+  const int dp = tid % DP, grp = tid / DP;
+  const int d = kMergeDims * dq + 2 * dp;
+  float2 acc = make_float2(0.0f, 0.0f);
+  float lsum = 0.0f;
+#pragma unroll 4
+  for (int s = grp; s < ns; s += ng) {
+    const float* p = part + (size_t)s * rec;
+    const float2 ml = *reinterpret_cast<const float2*>(p + D);
+    const float2 o = *reinterpret_cast<const float2*>(p + d);
+    const float f = __builtin_amdgcn_exp2f(ml.x - M);
+    acc.x = fmaf(o.x, f, acc.x);
+    acc.y = fmaf(o.y, f, acc.y);
+    lsum = fmaf(ml.y, f, lsum);
   }
-  const size_t gi = (size_t)b * a.Hq + h;
-  float gv, res;
-  if constexpr (sizeof(T) == 2) {
-    gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[gi]);
-    res = sigmoidf_dev(gv) * acc / lsum;
-    static_cast<uint16_t*>(a.out)[gi * D + d] = f32_to_bf16(res);
-  } else {
-    gv = static_cast<const float*>(a.gate)[gi];
-    res = (1.0f / (1.0f + expf(-gv))) * acc / lsum;
-    static_cast<float*>(a.out)[gi * D + d] = res;
+  gacc[tid] = acc;
+  gsum[tid] = lsum;
+  __syncthreads();
+  if (tid < DP) {
+    float2 r = gacc[tid];
+    float l = gsum[tid];
+    for (int g = 1; g < ng; ++g) {
+      const float2 x = gacc[g * DP + tid];
+      r.x += x.x;
+      r.y += x.y;
+      l += gsum[g * DP + tid];
+    }
+    const float gs = sigmoidf_dev(bf16_to_f32(static_cast<const uint16_t*>(a.gate)[bh])) / l;
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + (size_t)bh * D + d) =
+        pack_bf16x2(gs * r.x, gs * r.y);
   }
+}
+
+// Threads of a merge block: 16 per split group, 4 to 16 groups, enough for
+// every split to have a group of its own up to 16 splits.
+static int merge_threads(int num_splits) {
+  int ng = 4;
+  while (ng < 16 && ng < num_splits) ng *= 2;
+  return ng * (kMergeDims / 2);
 }
 
 // fp32: one wave per (sequence, query head), plain VALU arithmetic.
@@ -502,10 +545,13 @@ DecodePlan plan_decode(Elem e, int B, int Hq, int Hkv, int D, int sliding, int w
   }
   // Enough workgroups to fill the chip and balance unequal lengths, but no
   // split below kDecMinKeysPerBlock keys when there are many (sequence, KV
-  // head) pairs: short splits cost a merge pass that a 512-slot ring does
-  // not repay.
+  // head) pairs (short splits cost a merge pass that a 512-slot ring does
+  // not repay), nor below kDecMinKeysFewPairs otherwise: a split's fixed
+  // costs (q rotation, wave merge, partial) outweigh a shorter stream.
+  // Measured on one sequence: 65537 keys on 2 KV heads take 30 us in splits
+  // of 128 keys, 20 us in splits of 512 or 1024, 29 us in splits of 2048.
   long long splits = (kDecTargetBlocks + pairs - 1) / pairs;
-  const long long min_keys = pairs >= 256 ? kDecMinKeysPerBlock : kDecWaves * kChunk;
+  const long long min_keys = pairs >= 256 ? kDecMinKeysPerBlock : kDecMinKeysFewPairs;
   const long long max_splits = (n_vis_max + min_keys - 1) / min_keys;
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -530,7 +576,9 @@ hipError_t launch_decode(const DecodeArgs& a, Elem e, hipStream_t s) {
     hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(blocks), dim3(kDecThreads), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
-  hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3(a.B * a.Hq), dim3(a.D), 0, s, a);
+  static_assert(64 % kMergeDims == 0 && 128 % kMergeDims == 0, "whole dim groups");
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(a.B * a.Hq * (a.D / kMergeDims))),
+                     dim3(merge_threads(a.num_splits)), 0, s, a);
   return hipGetLastError();
 }
 

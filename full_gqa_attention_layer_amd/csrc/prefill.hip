@@ -812,25 +812,66 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
   if (lane + 64 < D) o[lane + 64] = o1 * f;
 }
 
-// Log-sum-exp merge of a chunk's key splits, then the gate: one block of D
-// threads per (sequence, row, head). Splits whose rows saw no key (reference
-// -inf) carry no weight.
-__global__ void prefill_merge_kernel(PrefillArgs a) {
+// Log-sum-exp merge of a chunk's key splits, then the gate. One block per
+// (sequence, row, head) of D/4 x NG threads: thread t takes dims 4 (t % (D/4))
+// .. + 3 and every NG-th split from t / (D/4); the NG split groups then add
+// up through LDS, so a call with many splits (one sequence's verify step
+// over a long context) is not one long dependent chain per thread. Splits
+// whose rows saw no key (reference -inf) carry no weight; every row sees at
+// least its own position, so some split has a finite reference.
+constexpr int kPMergeMaxThreads = 256;
+__global__ __launch_bounds__(kPMergeMaxThreads) void prefill_merge_kernel(PrefillArgs a) {
+  __shared__ float wave_max[kPMergeMaxThreads / 64];
+  __shared__ f32x4_t gacc[kPMergeMaxThreads];
+  __shared__ float gsum[kPMergeMaxThreads];
   const size_t row = blockIdx.x;  // (b T + t) Hq + h
-  const int D = a.D, d = threadIdx.x, ns = a.num_splits;
-  const float* pr = a.partial + row * ns * (D + 4);
+  const int D = a.D, ns = a.num_splits, rec = D + 4;  // record: D outputs, reference, sum, 2 spare
+  const int tid = threadIdx.x, nt = blockDim.x, DQ = D / 4, ng = nt / DQ;
+  const float* pr = a.partial + row * ns * rec;
+
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pr[s * (D + 4) + D]);
-  float acc = 0.0f, l = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    const float m = pr[s * (D + 4) + D];
-    if (m == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(m - M);
-    acc = fmaf(pr[s * (D + 4) + d], f, acc);
-    l = fmaf(pr[s * (D + 4) + D + 1], f, l);
+  for (int s = tid; s < ns; s += nt) M = fmaxf(M, pr[(size_t)s * rec + D]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if ((tid & 63) == 0) wave_max[tid >> 6] = M;
+  __syncthreads();
+  M = wave_max[0];
+  for (int w = 1; w < nt / 64; ++w) M = fmaxf(M, wave_max[w]);
+
+  const int dq = tid % DQ, grp = tid / DQ;
+  f32x4_t acc = {};
+  float l = 0.0f;
+  for (int s = grp; s < ns; s += ng) {
+    const float* p = pr + (size_t)s * rec;
+    const float2 ml = *reinterpret_cast<const float2*>(p + D);
+    if (ml.x == -INFINITY) continue;
+    const float f = __builtin_amdgcn_exp2f(ml.x - M);
+    acc += f * *reinterpret_cast<const f32x4_t*>(p + 4 * dq);
+    l = fmaf(ml.y, f, l);
   }
-  const float gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[row]);
-  static_cast<uint16_t*>(a.out)[row * D + d] = f32_to_bf16(sigmoidf_dev(gv) * acc / l);
+  gacc[tid] = acc;
+  gsum[tid] = l;
+  __syncthreads();
+  if (tid < DQ) {
+    f32x4_t r = gacc[tid];
+    float lt = gsum[tid];
+    for (int g = 1; g < ng; ++g) {
+      r += gacc[g * DQ + tid];
+      lt += gsum[g * DQ + tid];
+    }
+    const float gs = sigmoidf_dev(bf16_to_f32(static_cast<const uint16_t*>(a.gate)[row])) / lt;
+    const u32x2_t w = {pack_bf16x2(gs * r[0], gs * r[1]), pack_bf16x2(gs * r[2], gs * r[3])};
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(a.out) + row * D + 4 * tid) = w;
+  }
+}
+
+// Threads of a merge block: D/4 per split group, at least one wave, and
+// groups up to the split count (at most 256 threads).
+static int prefill_merge_threads(int num_splits, int D) {
+  const int dq = D / 4;
+  int ng = 64 / dq;
+  while (ng * dq < kPMergeMaxThreads && ng < num_splits) ng *= 2;
+  return ng * dq;
 }
 
 // Waves per workgroup. 8 (one workgroup per CU, each K/V tile copied once
@@ -921,8 +962,8 @@ hipError_t launch_prefill(const PrefillArgs& a, Elem e, hipStream_t s) {
   }
   err = hipGetLastError();
   if (err != hipSuccess || !cache || a.num_splits <= 1) return err;
-  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)((long long)a.B * a.T * a.Hq)), dim3(a.D), 0,
-                     s, a);
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((unsigned)((long long)a.B * a.T * a.Hq)),
+                     dim3(prefill_merge_threads(a.num_splits, a.D)), 0, s, a);
   return hipGetLastError();
 }
 

@@ -202,14 +202,14 @@ def test_decode_split_plan(lib):
     """The host split plan, seen through the workspace it asks for
     (B * Hq * splits * (D + 2) fp32, none for one split): the batched full
     layer takes 4 splits of 32768 keys, a 512-slot ring of 64 sequences one
-    split, and a lone short batch many splits of 128 keys."""
+    split, and a lone short batch many splits of 512 keys."""
     Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
     per_split = 64 * (128 + 2) * 4                      # one sequence, all heads
     assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 64, 131072) == 64 * 4 * per_split
     Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
     assert lib.attn_decode_workspace_bytes(ctypes.byref(Ls), 64, 131072) == 0
-    # 8 (sequence, KV head) pairs: aim for 2048 workgroups, at least 128 keys each
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 1 * 157 * per_split
+    # 8 (sequence, KV head) pairs: aim for 2048 workgroups, at least 512 keys each
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 1 * 40 * per_split
 
 
 def test_tuning_overrides(lib):
@@ -224,7 +224,7 @@ def test_tuning_overrides(lib):
         assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 0  # one split
     finally:
         assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 0) == hgqa.OK
-    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 157 * per_split
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(Lf), 1, 20000) == 40 * per_split
     assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, -1) == hgqa.EINVAL
     assert lib.hgqa_set_tuning(hgqa.TUNE_PREFILL_WAVES, 6) == hgqa.EINVAL
     assert lib.hgqa_set_tuning(hgqa.TUNE_CHUNK_SPLIT_TILES, -5) == hgqa.EINVAL

@@ -229,7 +229,7 @@ def test_decode_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("split_keys", [None, 128, 1024, 1 << 20])
+@pytest.mark.parametrize("split_keys", [None, 32, 128, 1024, 1 << 20])
 def test_split_counts_agree(split_keys, tuning):
     """The same decode with the keys cut into different split counts (the
     tuning override fixes the keys per split; 1 << 20 gives one split). Every
@@ -264,6 +264,46 @@ def test_split_counts_agree(split_keys, tuning):
 
 
 # ------------------------------------------------------------ full size
+
+@pytest.mark.parametrize("layer_index,split_keys", [(3, None), (3, 32), (0, None)])
+def test_single_sequence_after_muse_prompt(layer_index, split_keys, tuning):
+    """The decode step of the Muse block: one sequence, the token after a
+    65536-token prompt, 32 Q / 2 KV heads. The full layer (base 0) runs in
+    129 splits by default and in 2049 with 32-key splits (far more splits
+    than merge threads); the W = 2048 ring layer (base 5e5) in 4. The append
+    writes only slot L - 1 (or (L - 1) mod W), so the oracle's cache is the
+    GPU cache's other slots plus the oracle's own append of the new token."""
+    require_gpu()
+    wl = workloads.MUSE_BLOCK
+    shape = wl.layers[layer_index]
+    Lb = wl.seq_len + 1
+    Hkv, D = shape.num_kv_heads, shape.head_dim
+    cap = shape.window if shape.layer_type == SLIDING else Lb
+    key = (0, 960 + layer_index, 0)
+    kc = torch.empty(1, Hkv, cap, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    synth.device_normal_(kc, key + (synth.CACHE_K,))
+    synth.device_normal_(vc, key + (synth.CACHE_V,))
+    k_new = synth.host_normal((1, 1, Hkv, D), key + (synth.NEW_K,))
+    v_new = synth.host_normal((1, 1, Hkv, D), key + (synth.NEW_V,))
+    q = synth.host_normal((1, shape.num_q_heads, D), key + (synth.Q,))
+    g = synth.host_normal((1, shape.num_q_heads), key + (synth.GATE,))
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    if split_keys is not None:
+        tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, split_keys)
+    hgqa.kv_append(L, torch.full((1,), Lb - 1, dtype=torch.int32, device=DEV), Lb,
+                   k_new.to(DEV), v_new.to(DEV), kc, vc)
+    seq = torch.full((1,), Lb, dtype=torch.int32, device=DEV)
+    out = hgqa.attn_decode(L, q.to(DEV), g.to(DEV), kc, vc, seq, Lb)
+    torch.cuda.synchronize()
+    slot = (Lb - 1) % cap
+    okc, ovc = f64(kc), f64(vc)
+    okc[:, :, slot] = 0.0   # the oracle writes the new token itself
+    ovc[:, :, slot] = 0.0
+    okc, ovc = oracle.kv_append(okc, ovc, f64(k_new), f64(v_new), [Lb - 1], spec(shape))
+    ref = oracle.decode(f64(q), f64(g), okc, ovc, [Lb], spec(shape))
+    assert_close(out, ref, hgqa.BF16, f"Muse layer {layer_index} decode at {Lb}, split {split_keys}")
+
 
 def _c5_state(layer_index):
     """Caches, lengths and new-token inputs of the batched decode workload."""

@@ -50,8 +50,8 @@ def test_plan_larger_than_the_scratch_is_refused():
 
 
 CALLS = [
-    # shape, lengths: the first call splits every sequence (63 splits of 320
-    # keys, 8.4 MB of partials); the second is smaller (24 splits of 128 keys)
+    # shape, lengths: the first call splits every sequence (40 splits of 512
+    # keys, 5.3 MB of partials); the second is smaller (6 splits of 512 keys)
     (LayerShape(FULL, 0, 64, 8, 128, 5e6, 0.5), [5000, 20000, 1, 12000]),
     (LayerShape(FULL, 0, 16, 2, 128, 5e6, 0.5), [900, 3000]),
 ]
