@@ -157,6 +157,13 @@ size_t plan_splits(const Layer& l, hgqa::PrefillArgs& a, int max_end_pos) {
   a.k_cache = reinterpret_cast<const void*>(16);  // a chunk: the plan only tests for a cache
   a.sliding = l.sliding;
   a.window = l.window;
+  // The merge launches one block per row: no splits past the grid limit
+  // (reachable only through the split-tile override).
+  if ((long long)a.B * a.T * a.Hq > 0x7fffffffLL) {
+    a.num_splits = 1;
+    a.split_tiles = 0;
+    return 0;
+  }
   return round256(hgqa::plan_prefill_splits(a, l.elem, max_end_pos,
                                             g_chunk_split_tiles.load(std::memory_order_relaxed)));
 }
@@ -278,7 +285,10 @@ int hgqa::decode_call(const void* layer_ptr, int batch, const void* q, const voi
       return fail(HGQA_ENOSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
                   plan.workspace_bytes);
   }
-  if ((long long)batch * plan.num_splits * l.Hkv > 0x7fffffffLL)
+  // decode blocks, merge blocks (one per sequence, head and 32 dims), fp32 blocks
+  if ((long long)batch * plan.num_splits * l.Hkv > 0x7fffffffLL ||
+      (plan.num_splits > 1 && (long long)batch * l.Hq * (l.D / 32) > 0x7fffffffLL) ||
+      (long long)batch * l.Hq > 0x7fffffffLL)
     return fail(HGQA_EUNSUPPORTED, "too many decode blocks");
   hgqa::DecodeArgs a{};
   a.q = q;

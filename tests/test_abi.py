@@ -164,6 +164,41 @@ def test_prefill_chunk_workspace_formula(lib):
     assert ws(1, 4, 3) == 0                                  # max_end_pos below n_new
 
 
+def test_chunk_splits_stay_within_the_merge_grid(lib):
+    """The merge launches one block per row (B n Hq): a call with more rows than
+    a grid holds takes no key splits, even when the tuning override asks."""
+    Lf = hgqa.layer(0, 0, 64, 8, 128, 5e6, 0.5)
+    r256 = lambda x: (x + 255) // 256 * 256
+    n = 1 << 26                                    # 2^26 rows x 64 heads = 2^32
+    base = r256(8 * n * 128 * 2) + r256(n * 32 * 8)
+    try:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_CHUNK_SPLIT_TILES, 1) == hgqa.OK
+        assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), 1, n, n + 64) == base
+        # a small call still splits under the override
+        assert lib.attn_prefill_chunk_workspace_bytes(ctypes.byref(Lf), 1, 4, 1000) > \
+            r256(8 * 4 * 128 * 2) + r256(4 * 32 * 8)
+    finally:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_CHUNK_SPLIT_TILES, 0) == hgqa.OK
+
+
+def test_decode_merge_grid_limit(lib):
+    """Split decode merges in one block per (sequence, head, 32 dims): a call
+    whose merge grid would pass 2^31 - 1 blocks is refused before any launch
+    (reachable only through the split override: 65535 sequences of 32768 Q
+    heads, 64-slot caches cut into 32-key splits). Fake pointers."""
+    L = hgqa.layer(0, 0, 32768, 16, 128, 5e6, 0.5)
+    p = ctypes.c_void_p(4096)
+    o = ctypes.c_void_p(1 << 20)
+    try:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 32) == hgqa.OK
+        rc = lib.attn_decode(ctypes.byref(L), 65535, p, p, p, p, 64, p, 64, p,
+                             ctypes.c_size_t(1 << 50), o, None)
+        assert rc == hgqa.EUNSUPPORTED
+        assert "decode blocks" in hgqa.hgqa_last_error()
+    finally:
+        assert lib.hgqa_set_tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 0) == hgqa.OK
+
+
 def test_kv_append_argument_checks(lib):
     p = ctypes.c_void_p(256)
     Ls = hgqa.layer(1, 512, 64, 8, 128, 1e4)
