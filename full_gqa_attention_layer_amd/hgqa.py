@@ -135,7 +135,15 @@ def _need(t, name, shape, dtype):
 
 
 def _on_gpu(**tensors):
-    """After every shape is checked: each tensor must live on the GPU."""
+    """After every shape is checked: each tensor must live on the GPU. A
+    workspace (any dtype; the library sees its bytes) must also be one
+    contiguous block, since the library fills workspace_bytes from its start."""
+    ws = tensors.get("workspace")
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor):
+            raise TypeError("workspace must be a tensor")
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
     for name, t in tensors.items():
         if t is not None and not t.is_cuda:
             raise ValueError(f"{name} must be on the GPU")

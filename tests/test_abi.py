@@ -300,3 +300,12 @@ def test_binding_checks_shapes_against_the_descriptor(lib):
     with pytest.raises(ValueError, match="shape"):
         hgqa.attn_prefill(L, torch.zeros(1, 5, 16, 64, dtype=bf), torch.zeros(1, 5, 4, 64, dtype=bf),
                           torch.zeros(1, 5, 4, 64, dtype=bf), torch.zeros(1, 5, 16, dtype=bf))
+    # a workspace is one contiguous block (the library fills it from its start)
+    strided = torch.zeros(2, 1 << 16, dtype=torch.uint8)[:, ::2]
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        hgqa.attn_prefill(L, torch.zeros(1, 5, 16, 128, dtype=bf), torch.zeros(1, 5, 4, 128, dtype=bf),
+                          torch.zeros(1, 5, 4, 128, dtype=bf), torch.zeros(1, 5, 16, dtype=bf),
+                          workspace=strided)
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        hgqa.attn_decode(L, good["q"], good["g"], good["kc"], good["kc"].clone(), good["lens"], 10,
+                         workspace=strided)
