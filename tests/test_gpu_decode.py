@@ -229,8 +229,11 @@ def test_decode_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("split_keys", [None, 32, 128, 1024, 1 << 20])
-def test_split_counts_agree(split_keys, tuning):
+@pytest.mark.parametrize("shape,split_keys", [
+    (LayerShape(FULL, 0, 16, 2, 128, 5e6, 0.5), sk) for sk in (None, 32, 128, 1024, 1 << 20)] + [
+    # head_dim 64: two merge blocks of 32 dims per head
+    (LayerShape(FULL, 0, 8, 2, 64, 1e4, 0.25), sk) for sk in (None, 32)])
+def test_split_counts_agree(shape, split_keys, tuning):
     """The same decode with the keys cut into different split counts (the
     tuning override fixes the keys per split; 1 << 20 gives one split). Every
     plan matches the oracle. Against the one-split output the difference is
@@ -239,11 +242,11 @@ def test_split_counts_agree(split_keys, tuning):
     running maximum, so two plans differ by at most 2 * 2^-9 * sigmoid(gate) *
     max |v| over the sequence's keys, plus one bf16 step of the output."""
     require_gpu()
-    shape = LayerShape(FULL, 0, 16, 2, 128, 5e6, 0.5)
     lens = [1, 100, 4000, 20000]
     kc, vc, okc, ovc, _ = build_caches(shape, hgqa.BF16, lens, (0, 303, 0))
-    q = synth.host_normal((4, 16, 128), (0, 303, 0, synth.Q)).to(DEV)
-    g = synth.host_normal((4, 16), (0, 303, 0, synth.GATE)).to(DEV)
+    Hq, D = shape.num_q_heads, shape.head_dim
+    q = synth.host_normal((4, Hq, D), (0, 303, 0, synth.Q)).to(DEV)
+    g = synth.host_normal((4, Hq), (0, 303, 0, synth.GATE)).to(DEV)
     L = hgqa.layer_from_shape(shape, hgqa.BF16)
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
     tuning(hgqa.TUNE_DECODE_SPLIT_KEYS, 1 << 20)
@@ -252,7 +255,7 @@ def test_split_counts_agree(split_keys, tuning):
     out = hgqa.attn_decode(L, q, g, kc, vc, seq, max(lens))
     torch.cuda.synchronize()
     ref = oracle.decode(f64(q), f64(g), okc, ovc, lens, spec(shape))
-    assert_close(out, ref, hgqa.BF16, f"split_keys {split_keys}")
+    assert_close(out, ref, hgqa.BF16, f"D {D} split_keys {split_keys}")
     a, b = f64(out), f64(one)
     G = shape.num_q_heads // shape.num_kv_heads
     sig = 1.0 / (1.0 + np.exp(-f64(g)))                                   # [B, Hq]
