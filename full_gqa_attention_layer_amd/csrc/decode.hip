@@ -389,12 +389,38 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecodeArgs a) 
 }
 
 // Log-sum-exp merge of the splits of one (sequence, head), then the gate.
-// A long context alone can have hundreds of splits (a single sequence of
-// 64K keys on two KV heads: 129), so the splits are spread over the threads
-// too: one block per (sequence, head, 32 dims) of 16 x NG threads, where
-// thread t takes dims 2 (t % 16) and 2 (t % 16) + 1 of its 32 and every
-// NG-th split from t / 16; the NG split groups then add up through LDS. NG
-// (4, 8 or 16) follows the call's split count.
+// With a few splits (the batched decode's 4): one block of D threads per
+// (sequence, head), each thread looping over the splits for its dim.
+constexpr int kMergeFewSplits = 4;
+__global__ void decode_merge_few_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hq;
+  const int D = a.D, d = threadIdx.x;
+  int L = a.seq_lens[b];
+  L = max(1, min(L, a.max_seq_len));
+  const int n_vis = a.sliding ? min(L, a.window) : L;
+  const int ns = (n_vis + a.split_keys - 1) / a.split_keys;
+  const float* part = a.partial + (size_t)bh * a.num_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float acc = 0.0f, lsum = 0.0f;
+  for (int s = 0; s < ns; ++s) {
+    const float* p = part + s * (D + 2);
+    const float f = __builtin_amdgcn_exp2f(p[D] - M);
+    acc = fmaf(p[d], f, acc);
+    lsum = fmaf(p[D + 1], f, lsum);
+  }
+  const float gv = bf16_to_f32(static_cast<const uint16_t*>(a.gate)[bh]);
+  static_cast<uint16_t*>(a.out)[(size_t)bh * D + d] = f32_to_bf16(sigmoidf_dev(gv) * acc / lsum);
+}
+
+// With more splits (a long context alone has hundreds: a single sequence of
+// 64K keys on two KV heads, 129), one thread per dim looping over every split
+// is a chain of dependent L2 round trips, so the splits are spread over the
+// threads too: one block per (sequence, head, 32 dims) of 16 x NG threads
+// (NG = 4, 8 or 16, following the split count), where thread t takes dims
+// 2 (t % 16) and 2 (t % 16) + 1 of its 32 and every NG-th split from t / 16;
+// the NG split groups then add up through LDS.
 constexpr int kMergeDims = 32;
 constexpr int kMergeMaxThreads = 256;
 __global__ __launch_bounds__(kMergeMaxThreads) void decode_merge_kernel(DecodeArgs a) {
@@ -456,8 +482,7 @@ __global__ __launch_bounds__(kMergeMaxThreads) void decode_merge_kernel(DecodeAr
   }
 }
 
-// Threads of a merge block: 16 per split group, 4 to 16 groups, enough for
-// every split to have a group of its own up to 16 splits.
+// Threads of a many-split merge block: 16 per split group, 4 to 16 groups.
 static int merge_threads(int num_splits) {
   int ng = 4;
   while (ng < 16 && ng < num_splits) ng *= 2;
@@ -576,9 +601,13 @@ hipError_t launch_decode(const DecodeArgs& a, Elem e, hipStream_t s) {
     hipLaunchKernelGGL(decode_bf16_kernel<64>, dim3(blocks), dim3(kDecThreads), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.num_splits == 1) return err;
-  static_assert(64 % kMergeDims == 0 && 128 % kMergeDims == 0, "whole dim groups");
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(a.B * a.Hq * (a.D / kMergeDims))),
-                     dim3(merge_threads(a.num_splits)), 0, s, a);
+  if (a.num_splits <= kMergeFewSplits) {
+    hipLaunchKernelGGL(decode_merge_few_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(a.D), 0, s, a);
+  } else {
+    static_assert(64 % kMergeDims == 0 && 128 % kMergeDims == 0, "whole dim groups");
+    hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(a.B * a.Hq * (a.D / kMergeDims))),
+                       dim3(merge_threads(a.num_splits)), 0, s, a);
+  }
   return hipGetLastError();
 }
 
