@@ -214,6 +214,42 @@ def test_full_append_slot_is_position_and_leaves_other_slots():
     check_cache(kc, vc, okc, ovc, shape, hgqa.BF16, k_new, start.tolist())
 
 
+def test_out_of_range_device_lengths_and_starts_are_clamped():
+    """Device-side integers the host cannot check: decode clamps each
+    seq_lens[b] to [1, max_seq_len], and kv_append stores only the tokens
+    whose position falls in [0, cap). So a decode with lengths 0, 10^9 and -7
+    equals, bit for bit, one with 1, max_seq_len and 1; and an append that
+    starts at -5 writes tokens 5.. at slots 0.. and nothing else, as an
+    append of those tokens at 0 does."""
+    require_gpu()
+    shape = LayerShape(FULL, 0, 8, 2, 128, 5e6, 0.5)
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    lens = [1, 50, 300]
+    kc, vc, _, _, _ = build_caches(shape, hgqa.BF16, lens, (0, 304, 0))
+    q = synth.host_normal((3, 8, 128), (0, 304, 0, synth.Q)).to(DEV)
+    g = synth.host_normal((3, 8), (0, 304, 0, synth.GATE)).to(DEV)
+    bad = torch.tensor([0, 10 ** 9, -7], dtype=torch.int32, device=DEV)
+    good = torch.tensor([1, 300, 1], dtype=torch.int32, device=DEV)
+    a = hgqa.attn_decode(L, q, g, kc, vc, bad, 300)
+    b = hgqa.attn_decode(L, q, g, kc, vc, good, 300)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+    n, cap = 10, 64
+    k_new, v_new = _kv(shape, 1, n, hgqa.BF16, (0, 305, 0))
+    sentinel = torch.full((1, 2, cap, 128), -3.0, dtype=torch.bfloat16, device=DEV)
+    kc1, vc1 = sentinel.clone(), sentinel.clone()
+    kc2, vc2 = sentinel.clone(), sentinel.clone()
+    hgqa.kv_append(L, torch.tensor([-5], dtype=torch.int32, device=DEV), n, k_new.to(DEV),
+                   v_new.to(DEV), kc1, vc1)
+    hgqa.kv_append(L, torch.zeros(1, dtype=torch.int32, device=DEV), n - 5,
+                   k_new[:, 5:].contiguous().to(DEV), v_new[:, 5:].contiguous().to(DEV), kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(kc1.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc1.view(torch.int16), vc2.view(torch.int16))
+    assert torch.equal(kc1[:, :, n - 5:].view(torch.int16), sentinel[:, :, n - 5:].view(torch.int16))
+
+
 def test_decode_is_deterministic():
     require_gpu()
     shape = LayerShape(FULL, 0, 64, 8, 128, 5e6, 0.5)
