@@ -6,14 +6,17 @@ own p0. Its output must equal the plain prefill
 definition of the whole sequence at the chunk's rows (the oracle evaluates
 exactly those rows), and afterwards the cache must hold what kv_append of the
 whole sequence leaves (bit-exact). Chunks with n = 4 are the multi-token
-decode step (one token plus three drafts, causal among themselves).
+decode step (one token plus three drafts, causal among themselves). At the
+benchmark's sizes (a 2048-token chunk over 30720 cached tokens, the verify
+step over the batched decode's caches) sampled tokens are compared with
+one-token decodes of the oracle over the same history.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from full_gqa_attention_layer_amd import hgqa, synth
+from full_gqa_attention_layer_amd import hgqa, synth, workloads
 from full_gqa_attention_layer_amd.workloads import FULL, SLIDING, LayerShape
 from tests.gpu_helpers import DEV, assert_close, f64, prefill_inputs, require_gpu, spec, tdtype
 
@@ -160,3 +163,96 @@ def test_verify_step_automatic_splits():
     base = hgqa.attn_prefill_chunk_workspace_bytes(L, 3, 4, 4)  # no split for 4 keys
     assert hgqa.attn_prefill_chunk_workspace_bytes(L, 3, 4, 9000) > base
     _chunk_case(shape, hgqa.BF16, [8996, 5000, 123], 4, 40)
+
+
+# ------------------------------------------------------------ full size
+#
+# The benchmark's chunk and verify legs at their own sizes. The caches hold
+# seeded random (already rotated) keys, so the reference for a new token is a
+# one-token decode at its position over the oracle's cache: the slots below
+# the chunk's start as given, then the oracle's own append of the chunk.
+
+def _oracle_cache(kc, vc, b, p0, k_new, v_new, shape):
+    """Sequence b's cache for the oracle: slots [0, p0) copied from the GPU
+    cache (inputs the call leaves alone), the new tokens appended by the
+    oracle at p0.."""
+    n = k_new.shape[1]
+    okc = np.zeros((1, kc.shape[1], p0 + n, kc.shape[3]))
+    ovc = np.zeros_like(okc)
+    okc[:, :, :p0] = f64(kc[b:b + 1, :, :p0])
+    ovc[:, :, :p0] = f64(vc[b:b + 1, :, :p0])
+    return oracle.kv_append(okc, ovc, f64(k_new[b:b + 1]), f64(v_new[b:b + 1]), [p0], spec(shape))
+
+
+def test_chunked_prefill_full_size():
+    """2048 new tokens at positions 30720.. of the Step full layer (64 Q / 8 KV,
+    base 5e6, rotary 0.5), the benchmark's chunk: sampled tokens (the first
+    and last, both sides of 64-key tile edges, seeded others), every head."""
+    require_gpu()
+    shape = workloads.STEP_FULL.layers[0]
+    Hq, Hkv, D = shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    p0, n = 30720, 2048
+    key = (0, 970, 0)
+    kc = torch.empty(1, Hkv, p0 + n, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    synth.device_normal_(kc, key + (synth.CACHE_K,))
+    synth.device_normal_(vc, key + (synth.CACHE_V,))
+    q = synth.host_normal((1, n, Hq, D), key + (synth.Q,))
+    k = synth.host_normal((1, n, Hkv, D), key + (synth.K,))
+    v = synth.host_normal((1, n, Hkv, D), key + (synth.V,))
+    g = synth.host_normal((1, n, Hq), key + (synth.GATE,))
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    out = hgqa.attn_prefill_chunk(L, p0, q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), kc, vc)
+    torch.cuda.synchronize()
+    okc, ovc = _oracle_cache(kc, vc, 0, p0, k, v, shape)
+    rng = np.random.default_rng(11)
+    rows = sorted({0, 1, 63, 64, 65, 1023, 1024, n - 2, n - 1} |
+                  {int(t) for t in rng.integers(0, n, 7)})
+    got = np.stack([f64(out[0, t]) for t in rows])
+    ref = np.stack([oracle.decode(f64(q[:, t]), f64(g[:, t]), okc, ovc, [p0 + t + 1],
+                                  spec(shape))[0] for t in rows])
+    assert_close(got, ref, hgqa.BF16, f"chunk of {n} over {p0}: tokens {rows}")
+
+
+def test_verify_step_full_size():
+    """The benchmark's verify step: 64 sequences over the batched decode's
+    full-layer caches (lengths U[65536, 131072]), 4 new tokens each (1 + 3
+    drafts) ending at position L_b - 1. The shortest and the longest sequence
+    and four seeded others, every token and head, one sequence at a time so
+    host memory stays bounded."""
+    require_gpu()
+    wl = workloads.BATCHED_DECODE
+    shape = wl.layers[0]
+    B, Hq, Hkv, D, n = wl.batch, shape.num_q_heads, shape.num_kv_heads, shape.head_dim, 4
+    lens = synth.host_uniform_int(wl.min_seq_len, wl.seq_len, B, (0, wl.wid, 0, synth.SEQ_LENS))
+    key = (0, 971, 0)
+    kc = torch.empty(B, Hkv, wl.seq_len, D, dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    for b in range(B):
+        synth.device_normal_(kc[b], key + (synth.CACHE_K, b))
+        synth.device_normal_(vc[b], key + (synth.CACHE_V, b))
+    q = synth.host_normal((B, n, Hq, D), key + (synth.Q,))
+    g = synth.host_normal((B, n, Hq), key + (synth.GATE,))
+    kn = synth.host_normal((B, n, Hkv, D), key + (synth.NEW_K,))
+    vn = synth.host_normal((B, n, Hkv, D), key + (synth.NEW_V,))
+    starts = lens - n
+    L = hgqa.layer_from_shape(shape, hgqa.BF16)
+    out = hgqa.attn_prefill_chunk(L, torch.tensor(starts, dtype=torch.int32, device=DEV),
+                                  q.to(DEV), kn.to(DEV), vn.to(DEV), g.to(DEV), kc, vc,
+                                  max_end_pos=int(lens.max()))
+    torch.cuda.synchronize()
+    order = np.argsort(lens)
+    rng = np.random.default_rng(12)
+    picks = sorted({int(order[0]), int(order[-1])} |
+                   {int(b) for b in rng.permutation(order[1:-1])[:4]})
+    got, ref = [], []
+    for b in picks:
+        p0 = int(starts[b])
+        okc, ovc = _oracle_cache(kc, vc, b, p0, kn, vn, shape)
+        for t in range(n):
+            ref.append(oracle.decode(f64(q[b:b + 1, t]), f64(g[b:b + 1, t]), okc, ovc,
+                                     [p0 + t + 1], spec(shape))[0])
+            got.append(f64(out[b, t]))
+        del okc, ovc
+    assert_close(np.stack(got), np.stack(ref), hgqa.BF16,
+                 f"verify step over lengths {int(lens.min())}..{int(lens.max())}: sequences {picks}")
